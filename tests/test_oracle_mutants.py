@@ -1,0 +1,59 @@
+"""Planted mistakes in the oracle (on the CPU) must each be caught by at least one pin.
+
+Every mutant is a fresh copy of ``oracle/attention.py`` with one plausible bug written into
+its source text (a dropped term, a wrong sign or index, a transposed operand).  Each must
+fail at least one pin, which shows the pins constrain every part of the oracle.
+"""
+import os
+import types
+
+import pytest
+
+from tests import oracle_pins
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = open(os.path.join(ROOT, "oracle", "attention.py"), encoding="utf-8").read()
+
+# (name, exact text in the oracle, planted replacement)
+MUTANTS = [
+    ("inv_freq_missing_two", "-2.0 * i / dim", "-1.0 * i / dim"),
+    ("rope_sign", "ra = a * c - b * s", "ra = a * c + b * s"),
+    ("rope_inverse_ignored", "        s = -s\n", "        s = s\n"),
+    ("rope_pairs_swapped", 'a, b = x[..., : D // 2], x[..., D // 2:]', 'b, a = x[..., : D // 2], x[..., D // 2:]'),
+    ("strict_causal", "gk[None, :] <= gq[:, None]", "gk[None, :] < gq[:, None]"),
+    ("offsets_swapped", "gq = np.asarray(rows, dtype=np.int64) + int(q_offset)",
+     "gq = np.asarray(rows, dtype=np.int64) + int(k_offset)"),
+    ("no_segment_mask", "vis &= np.asarray(seg_q_row)[rows][:, None] == np.asarray(seg_k_row)[None, :]", "pass"),
+    ("scale_default_dropped", "scale = 1.0 / math.sqrt(D) if scale is None else float(scale)\n    rows",
+     "scale = 1.0 if scale is None else float(scale)\n    rows"),
+    ("max_not_subtracted_from_lse", "m + np.log(np.where(has, l, 1.0))", "np.log(np.where(has, l, 1.0))"),
+    ("lse_log2", "m + np.log(np.where(has, l, 1.0))", "m + np.log2(np.where(has, l, 1.0))"),
+    ("bwd_rowsum_term_dropped", "ds = p * (dp - d_i[:, None])", "ds = p * dp"),
+    ("bwd_dv_uses_dq_side", "dvh[:lim] += p.T @ dob", "dvh[:lim] += p.T @ qb"),
+    ("bwd_dk_transposed_operand", "dkh[:lim] += scale * (ds.T @ qb)", "dkh[:lim] += scale * (ds.T @ dob)"),
+    ("bwd_dq_missing_scale", "dq[b, rr, h, :] = scale * (ds @ kh[:lim])", "dq[b, rr, h, :] = ds @ kh[:lim]"),
+    ("merge_weights_swapped", "return ca * np.asarray(o_a, dtype=np.float64) + cb * np.asarray(o_b",
+     "return cb * np.asarray(o_a, dtype=np.float64) + ca * np.asarray(o_b"),
+    ("segment_positions_not_restarting", "                start = t\n", "                start = 0\n"),
+    ("training_inverse_rope_forgotten", "dq = rope(dqr, pos_q, theta, layout, inverse=True)",
+     "dq = rope(dqr, pos_q, theta, layout)"),
+]
+
+
+def mutant(old, new):
+    assert SRC.count(old) >= 1, f"mutation anchor vanished: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(SRC.replace(old, new, 1), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(name, old, new):
+    mod = mutant(old, new)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(mod)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught the planted mistake {name}"
