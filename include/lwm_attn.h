@@ -1,0 +1,163 @@
+/*
+ * lwm_attn.h - C ABI of the MI355X (gfx950) blockwise causal ring-attention library.
+ *
+ * What the library computes, and where the pages state it:
+ *
+ *  - RoPE with theta scaled to the context length: "[论文解读] World Model on Million-Length
+ *    Video And Language With Blockwise RingAttention", section 提出的方法 (theta is a per-model
+ *    setting; "LWM：突破 100 万 Token 的开源大模型", section 脚本运行说明, shows theta=50000000).
+ *  - Self-attention computed blockwise over query and key chunks: "LWM：突破 100 万 Token 的
+ *    开源大模型", section 配置参数 (scan_query_chunk_size / scan_key_chunk_size).
+ *  - Autoregressive (causal) attention: "Inside Large World Model: UC Berkeley Multimodal
+ *    Model that can Understand 1 Hour Long Videos", section "Core Architecture".
+ *  - Masked sequence packing (segments of one packed row attend only within themselves):
+ *    "LWM：突破 100 万 Token 的开源大模型", section 概述, item (b).
+ *  - RingAttention: KV blocks travel around a ring of devices while each keeps its query
+ *    block, compute overlapping transfer: "开源巨兽LWM：如何用RingAttention撬动百万Token多模态
+ *    世界", section 3.1; sequence-parallel mesh axis: "LWM：突破 100 万 Token 的开源大模型",
+ *    section 配置参数.  One ring step folds one KV shard into a running (O, logsumexp) state.
+ *
+ * The pages give no formula.  The library computes, per batch b and head h, for query i
+ * (global index q_offset + i) and key j (global index k_offset + j):
+ *     visible(i, j) = (!causal || k_offset + j <= q_offset + i) && (seg_q[i] == seg_k[j])
+ *     S_ij = scale * <Q'_i, K'_j>,   P = softmax over visible j,   O_i = sum_j P_ij V_j,
+ *     lse_i = ln sum_{visible j} exp(S_ij)          (natural log, float32)
+ * A row with no visible key gets O = 0 and lse = -inf.  Q' and K' are the RoPE-rotated
+ * operands: callers apply lwm_rope_apply first.
+ *
+ * Conventions for every entry point:
+ *  - Tensors are described by lwm_tensor4: element strides sB, sL, sH; the D (feature)
+ *    stride is 1.  The data pointer is device memory (hipMalloc / torch CUDA tensors) and must
+ *    be 16-byte aligned; sB, sL, sH must be multiples of 16 bytes worth of elements (8 for bf16,
+ *    4 for fp32).  Segment-id and position arrays are device int32 [B, L], contiguous.
+ *    lse arrays are device float32 [B, H, Lq], contiguous.
+ *  - The caller owns every buffer (including the backward workspace).  The library allocates
+ *    no device memory and keeps no state besides its code objects and a thread-local error
+ *    string.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  All work is enqueued
+ *    asynchronously on it; inputs must stay alive until it completes.
+ *  - Arguments are validated on the host before anything is launched.  A failed check
+ *    returns a negative lwm_status, launches nothing, and leaves a message readable through
+ *    lwm_last_error() on the calling thread.  Faults inside kernels surface at the caller's
+ *    next synchronisation of `stream`.
+ *  - Segment ids must be non-decreasing along each row (contiguous packing).  The mask
+ *    itself is evaluated element by element, but the key-tile range each query tile visits
+ *    is found by binary search, so other id orders give unspecified (memory-safe) results.
+ *  - Outputs must not overlap inputs, except that lwm_rope_apply may run in place (y == x).
+ */
+#ifndef LWM_ATTN_H
+#define LWM_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LWM_ABI_VERSION 1
+
+typedef enum {
+  LWM_OK = 0,
+  LWM_ERR_INVALID_ARG = -1, /* null pointer, shape/stride mismatch, misalignment, bad value */
+  LWM_ERR_UNSUPPORTED = -2, /* valid request the kernels do not implement (e.g. D != 128)     */
+  LWM_ERR_WORKSPACE = -3,   /* backward workspace missing or smaller than required           */
+  LWM_ERR_HIP = -4          /* the HIP runtime refused a launch; message has its error text  */
+} lwm_status;
+
+typedef enum { LWM_BF16 = 0, LWM_FP32 = 1 } lwm_dtype;
+
+typedef enum {
+  LWM_ROPE_HALF = 0,        /* feature i pairs with i + D/2 (LLaMA / HF convention, default) */
+  LWM_ROPE_INTERLEAVED = 1  /* feature 2i pairs with 2i + 1                                 */
+} lwm_rope_layout;
+
+/* A [B, L, H, D] tensor view.  Element strides; the D stride is 1. */
+typedef struct lwm_tensor4 {
+  void* ptr;
+  int32_t dtype; /* lwm_dtype */
+  int32_t reserved;
+  int64_t B, L, H, D;
+  int64_t sB, sL, sH;
+} lwm_tensor4;
+
+/* Version of this ABI (LWM_ABI_VERSION of the built library). */
+int lwm_abi_version(void);
+
+/* Message of the last failed call on this thread; "" after a successful call. Never NULL. */
+const char* lwm_last_error(void);
+
+/*
+ * RoPE (theta scaled to context length; see the header comment for the source).
+ * For every token t of batch row b the position is
+ *     p = pos_offset + (pos ? pos[b*L + t] : seg ? t - first(b, t) : t)
+ * where first(b, t) is the index of the first token of t's segment (positions restart at
+ * each packed segment).  inv_freq_i = theta^(-2i/D); the angle p * inv_freq_i is formed and
+ * reduced modulo 2*pi in double precision, its sine and cosine taken in single precision.
+ * Each pair (x_a, x_b) (layout selects the pairing) becomes
+ *     (x_a cos - x_b sin,  x_a sin + x_b cos)       (inverse != 0: rotate by -angle).
+ * x, y: same dtype (bf16: result rounded to nearest even; fp32) and shape [B, L, H, D] with
+ * D even, 16 <= D <= 256, D % 16 == 0.  y may be x (in place).  theta > 0.
+ */
+int lwm_rope_apply(const lwm_tensor4* x, const lwm_tensor4* y, const int32_t* pos,
+                   const int32_t* seg, int64_t pos_offset, double theta, int32_t layout,
+                   int32_t inverse, void* stream);
+
+/*
+ * Blockwise attention forward: O = softmax(scale * Q K^T + mask) V and lse (natural log).
+ * q [B, Lq, H, 128], k and v [B, Lk, H, 128], o [B, Lq, H, 128]: all bf16, or all fp32.
+ * seg_q [B, Lq] and seg_k [B, Lk] are both NULL (one segment) or both given.
+ * q_offset / k_offset: global index of the first query / key (>= 0).  causal: 0 or 1.
+ * scale: > 0, or 0 for 1/sqrt(D).  lse: float32 [B, H, Lq] (NULL to skip).
+ * bf16 path: P is rounded to bf16 before P*V, every sum is accumulated in float32, and O is
+ * rounded to bf16 at the end.  fp32 path: float32 throughout.
+ */
+int lwm_blockattn_fwd(const lwm_tensor4* q, const lwm_tensor4* k, const lwm_tensor4* v,
+                      const int32_t* seg_q, const int32_t* seg_k, int64_t q_offset,
+                      int64_t k_offset, int32_t causal, float scale, const lwm_tensor4* o,
+                      float* lse, void* stream);
+
+/* Bytes of workspace lwm_blockattn_bwd needs for these sizes (a multiple of 256). */
+size_t lwm_blockattn_bwd_workspace_size(int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D);
+
+/*
+ * Blockwise attention backward (bf16 only), for the loss sum(dout * O):
+ *     D_i = sum_d dout_id O_id,  P = exp(S - lse),  dV = P^T dout,  dP = dout V^T,
+ *     dS = P o (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
+ * q, k, v, seg_*, offsets, causal, scale as in lwm_blockattn_fwd; o and lse are that call's
+ * outputs; dout like o.  dq [B, Lq, H, 128], dk and dv [B, Lk, H, 128] (bf16) are written
+ * (not accumulated) and are gradients w.r.t. the operands given (the rotated Q', K'); apply
+ * lwm_rope_apply(inverse=1) to dq and dk for gradients w.r.t. the pre-RoPE Q and K.
+ * workspace: device memory of at least lwm_blockattn_bwd_workspace_size() bytes, 256-byte
+ * aligned; its contents on entry do not matter.
+ */
+int lwm_blockattn_bwd(const lwm_tensor4* q, const lwm_tensor4* k, const lwm_tensor4* v,
+                      const lwm_tensor4* o, const float* lse, const lwm_tensor4* dout,
+                      const int32_t* seg_q, const int32_t* seg_k, int64_t q_offset,
+                      int64_t k_offset, int32_t causal, float scale, const lwm_tensor4* dq,
+                      const lwm_tensor4* dk, const lwm_tensor4* dv, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/*
+ * One ring step (bf16): fold KV shard (k_shard, v_shard) into the running state of the
+ * query block.  The state is the normalised partial output o_acc (float32 [B, Lq, H, 128],
+ * described by a lwm_tensor4 of dtype LWM_FP32) and lse_acc (float32 [B, H, Lq]); before the
+ * first step the caller sets o_acc = 0 and lse_acc = -inf.  After the step they hold exactly
+ * (up to rounding) the attention of each query over all keys folded in so far:
+ *     lse' = ln(e^lse + e^lse_shard),  o' = e^(lse - lse') o + e^(lse_shard - lse') o_shard.
+ * Rows that see no key of this shard keep their state bit for bit.  k_offset is the global
+ * index of the shard's first key; seg_*, causal, scale as in lwm_blockattn_fwd.  o_final:
+ * NULL, or a bf16 [B, Lq, H, 128] view that receives the merged state rounded to bf16 (pass
+ * it on the last step).  Shards that are entirely in the causal future may be skipped by the
+ * caller; passing them is a valid no-op for the state.
+ */
+int lwm_ring_step(const lwm_tensor4* q, const lwm_tensor4* k_shard, const lwm_tensor4* v_shard,
+                  const int32_t* seg_q, const int32_t* seg_k, int64_t q_offset, int64_t k_offset,
+                  int32_t causal, float scale, const lwm_tensor4* o_acc, float* lse_acc,
+                  const lwm_tensor4* o_final, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LWM_ATTN_H */

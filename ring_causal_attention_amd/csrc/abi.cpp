@@ -1,0 +1,236 @@
+// C ABI of the library: argument validation on the host, then dispatch to the gfx950 kernels.
+// Every check runs before anything is launched; a failed check returns a negative status and
+// leaves a message for lwm_last_error() on the calling thread.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/lwm_attn.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return LWM_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(LWM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t elem_size(int32_t dtype) { return dtype == LWM_BF16 ? 2 : 4; }
+
+// Shape, stride and alignment rules shared by every tensor argument.
+int check_tensor(const lwm_tensor4* t, const char* name) {
+  if (!t) return fail(LWM_ERR_INVALID_ARG, "%s: descriptor is NULL", name);
+  if (t->dtype != LWM_BF16 && t->dtype != LWM_FP32) return fail(LWM_ERR_UNSUPPORTED, "%s: unknown dtype %d", name, t->dtype);
+  if (t->B < 0 || t->L < 0 || t->H < 0 || t->D < 0) return fail(LWM_ERR_INVALID_ARG, "%s: negative size", name);
+  if (t->B > 65535 || t->L > (int64_t(1) << 30) || t->H > 65535)
+    return fail(LWM_ERR_UNSUPPORTED, "%s: sizes beyond B<=65535, L<=2^30, H<=65535", name);
+  const int64_t vec = 16 / (int64_t)elem_size(t->dtype);
+  if (t->sB % vec || t->sL % vec || t->sH % vec)
+    return fail(LWM_ERR_INVALID_ARG, "%s: strides must be multiples of %lld elements (16 bytes)", name, (long long)vec);
+  if (t->sB < 0 || t->sL < 0 || t->sH < 0) return fail(LWM_ERR_INVALID_ARG, "%s: negative stride", name);
+  const bool empty = t->B == 0 || t->L == 0 || t->H == 0;
+  if (!empty) {
+    if (!t->ptr) return fail(LWM_ERR_INVALID_ARG, "%s: data pointer is NULL", name);
+    if (reinterpret_cast<uintptr_t>(t->ptr) % 16) return fail(LWM_ERR_INVALID_ARG, "%s: data pointer not 16-byte aligned", name);
+    if (t->sH < t->D && t->H > 1) return fail(LWM_ERR_INVALID_ARG, "%s: head stride overlaps features", name);
+  }
+  return LWM_OK;
+}
+
+int check_same(const lwm_tensor4* a, const lwm_tensor4* b, const char* an, const char* bn, bool same_L) {
+  if (a->dtype != b->dtype) return fail(LWM_ERR_UNSUPPORTED, "%s and %s: mixed dtypes", an, bn);
+  if (a->B != b->B || a->H != b->H || a->D != b->D || (same_L && a->L != b->L))
+    return fail(LWM_ERR_INVALID_ARG, "%s [%lld,%lld,%lld,%lld] and %s [%lld,%lld,%lld,%lld]: shape mismatch", an,
+                (long long)a->B, (long long)a->L, (long long)a->H, (long long)a->D, bn, (long long)b->B,
+                (long long)b->L, (long long)b->H, (long long)b->D);
+  return LWM_OK;
+}
+
+lwm::Strides strides(const lwm_tensor4* t) { return lwm::Strides{t->sB, t->sL, t->sH}; }
+
+int check_scale(float scale, int64_t D, float* scale_out) {
+  if (!std::isfinite(scale) || scale < 0.f) return fail(LWM_ERR_INVALID_ARG, "scale must be finite and >= 0 (0 = 1/sqrt(D))");
+  *scale_out = scale == 0.f ? (float)(1.0 / std::sqrt((double)D)) : scale;
+  return LWM_OK;
+}
+
+// Checks common to forward, backward and ring step; fills the shared part of the parameters.
+int check_attention(const lwm_tensor4* q, const lwm_tensor4* k, const lwm_tensor4* v, const int32_t* seg_q,
+                    const int32_t* seg_k, int64_t q_offset, int64_t k_offset, int32_t causal) {
+  int s;
+  if ((s = check_tensor(q, "q")) || (s = check_tensor(k, "k")) || (s = check_tensor(v, "v"))) return s;
+  if ((s = check_same(q, k, "q", "k", false)) || (s = check_same(k, v, "k", "v", true))) return s;
+  if (q->D != lwm::kHeadDim) return fail(LWM_ERR_UNSUPPORTED, "head dimension %lld: only 128 is implemented", (long long)q->D);
+  if ((seg_q == nullptr) != (seg_k == nullptr)) return fail(LWM_ERR_INVALID_ARG, "seg_q and seg_k must both be given or both NULL");
+  if (q_offset < 0 || k_offset < 0 || q_offset > (int64_t(1) << 40) || k_offset > (int64_t(1) << 40))
+    return fail(LWM_ERR_INVALID_ARG, "offsets must be in [0, 2^40]");
+  if (causal != 0 && causal != 1) return fail(LWM_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if ((q->B * q->H) > (int64_t(1) << 31) / ((q->L + 127) / 128 + 1)) return fail(LWM_ERR_UNSUPPORTED, "grid too large");
+  return LWM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lwm_abi_version(void) { return LWM_ABI_VERSION; }
+
+const char* lwm_last_error(void) { return g_err; }
+
+int lwm_rope_apply(const lwm_tensor4* x, const lwm_tensor4* y, const int32_t* pos, const int32_t* seg,
+                   int64_t pos_offset, double theta, int32_t layout, int32_t inverse, void* stream) {
+  int s;
+  if ((s = check_tensor(x, "x")) || (s = check_tensor(y, "y"))) return s;
+  if ((s = check_same(x, y, "x", "y", true))) return s;
+  if (x->D < 16 || x->D > 2 * lwm::kMaxRopeHalf || x->D % 16)
+    return fail(LWM_ERR_UNSUPPORTED, "RoPE feature size %lld: need 16 <= D <= 256, D %% 16 == 0", (long long)x->D);
+  if (!(theta > 0.0) || !std::isfinite(theta)) return fail(LWM_ERR_INVALID_ARG, "theta must be finite and > 0");
+  if (layout != LWM_ROPE_HALF && layout != LWM_ROPE_INTERLEAVED) return fail(LWM_ERR_INVALID_ARG, "unknown RoPE layout %d", layout);
+  if (inverse != 0 && inverse != 1) return fail(LWM_ERR_INVALID_ARG, "inverse must be 0 or 1");
+  if (pos_offset < -(int64_t(1) << 40) || pos_offset > (int64_t(1) << 40)) return fail(LWM_ERR_INVALID_ARG, "pos_offset out of range");
+  if (x->ptr == y->ptr && (x->sB != y->sB || x->sL != y->sL || x->sH != y->sH))
+    return fail(LWM_ERR_INVALID_ARG, "in-place RoPE needs identical strides");
+  lwm::RopeParams p{};
+  p.x = x->ptr;
+  p.y = y->ptr;
+  p.pos = pos;
+  p.seg = pos ? nullptr : seg;
+  p.pos_offset = pos_offset;
+  p.B = (int)x->B;
+  p.L = (int)x->L;
+  p.H = (int)x->H;
+  p.D = (int)x->D;
+  p.xsB = x->sB; p.xsL = x->sL; p.xsH = x->sH;
+  p.ysB = y->sB; p.ysL = y->sL; p.ysH = y->sH;
+  p.layout = layout;
+  p.inverse = inverse;
+  for (int i = 0; i < p.D / 2; ++i) p.inv_freq[i] = std::pow(theta, -2.0 * i / (double)p.D);
+  return hip_status(lwm::launch_rope(p, x->dtype == LWM_BF16, static_cast<hipStream_t>(stream)), "rope launch");
+}
+
+int lwm_blockattn_fwd(const lwm_tensor4* q, const lwm_tensor4* k, const lwm_tensor4* v, const int32_t* seg_q,
+                      const int32_t* seg_k, int64_t q_offset, int64_t k_offset, int32_t causal, float scale,
+                      const lwm_tensor4* o, float* lse, void* stream) {
+  int s;
+  if ((s = check_attention(q, k, v, seg_q, seg_k, q_offset, k_offset, causal))) return s;
+  if ((s = check_tensor(o, "o")) || (s = check_same(q, o, "q", "o", true))) return s;
+  float sc;
+  if ((s = check_scale(scale, q->D, &sc))) return s;
+  if (lse && reinterpret_cast<uintptr_t>(lse) % 4) return fail(LWM_ERR_INVALID_ARG, "lse not 4-byte aligned");
+  lwm::FwdParams p{};
+  p.q = q->ptr; p.k = k->ptr; p.v = v->ptr;
+  p.sq = strides(q); p.sk = strides(k); p.sv = strides(v);
+  p.B = (int)q->B; p.H = (int)q->H; p.Lq = (int)q->L; p.Lk = (int)k->L;
+  p.seg_q = seg_q; p.seg_k = seg_k;
+  p.q_offset = q_offset; p.k_offset = k_offset; p.causal = causal;
+  p.scale_log2 = sc * 1.4426950408889634f;
+  p.o = o->ptr; p.so = strides(o);
+  p.lse = lse;
+  p.mode = 0;
+  return hip_status(lwm::launch_attn_fwd(p, q->dtype == LWM_BF16, static_cast<hipStream_t>(stream)), "forward launch");
+}
+
+size_t lwm_blockattn_bwd_workspace_size(int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D) {
+  (void)Lk;
+  (void)D;
+  if (B <= 0 || H <= 0 || Lq <= 0) return 256;
+  const size_t delta = (size_t)B * (size_t)H * (size_t)Lq * sizeof(float);
+  return (delta + 255) / 256 * 256;
+}
+
+int lwm_blockattn_bwd(const lwm_tensor4* q, const lwm_tensor4* k, const lwm_tensor4* v, const lwm_tensor4* o,
+                      const float* lse, const lwm_tensor4* dout, const int32_t* seg_q, const int32_t* seg_k,
+                      int64_t q_offset, int64_t k_offset, int32_t causal, float scale, const lwm_tensor4* dq,
+                      const lwm_tensor4* dk, const lwm_tensor4* dv, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  int s;
+  if ((s = check_attention(q, k, v, seg_q, seg_k, q_offset, k_offset, causal))) return s;
+  if (q->dtype != LWM_BF16) return fail(LWM_ERR_UNSUPPORTED, "backward is implemented for bf16 only");
+  if ((s = check_tensor(o, "o")) || (s = check_same(q, o, "q", "o", true))) return s;
+  if ((s = check_tensor(dout, "dout")) || (s = check_same(q, dout, "q", "dout", true))) return s;
+  if ((s = check_tensor(dq, "dq")) || (s = check_same(q, dq, "q", "dq", true))) return s;
+  if ((s = check_tensor(dk, "dk")) || (s = check_same(k, dk, "k", "dk", true))) return s;
+  if ((s = check_tensor(dv, "dv")) || (s = check_same(v, dv, "v", "dv", true))) return s;
+  float sc;
+  if ((s = check_scale(scale, q->D, &sc))) return s;
+  const bool empty = q->B == 0 || q->H == 0 || (q->L == 0 && k->L == 0);
+  if (!empty && !lse && q->L > 0) return fail(LWM_ERR_INVALID_ARG, "lse is NULL");
+  const size_t need = lwm_blockattn_bwd_workspace_size(q->B, q->H, q->L, k->L, q->D);
+  if (!empty && (!workspace || workspace_bytes < need))
+    return fail(LWM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  if (workspace && reinterpret_cast<uintptr_t>(workspace) % 256) return fail(LWM_ERR_WORKSPACE, "workspace not 256-byte aligned");
+  lwm::BwdParams p{};
+  p.q = static_cast<const uint16_t*>(q->ptr);
+  p.k = static_cast<const uint16_t*>(k->ptr);
+  p.v = static_cast<const uint16_t*>(v->ptr);
+  p.o = static_cast<const uint16_t*>(o->ptr);
+  p.dout = static_cast<const uint16_t*>(dout->ptr);
+  p.sq = strides(q); p.sk = strides(k); p.sv = strides(v); p.so = strides(o); p.sdo = strides(dout);
+  p.lse = lse;
+  p.delta = static_cast<float*>(workspace);
+  p.B = (int)q->B; p.H = (int)q->H; p.Lq = (int)q->L; p.Lk = (int)k->L;
+  p.seg_q = seg_q; p.seg_k = seg_k;
+  p.q_offset = q_offset; p.k_offset = k_offset; p.causal = causal;
+  p.scale = sc;
+  p.scale_log2 = sc * 1.4426950408889634f;
+  p.dq = static_cast<uint16_t*>(dq->ptr);
+  p.dk = static_cast<uint16_t*>(dk->ptr);
+  p.dv = static_cast<uint16_t*>(dv->ptr);
+  p.sdq = strides(dq); p.sdk = strides(dk); p.sdv = strides(dv);
+  return hip_status(lwm::launch_attn_bwd(p, static_cast<hipStream_t>(stream)), "backward launch");
+}
+
+int lwm_ring_step(const lwm_tensor4* q, const lwm_tensor4* k_shard, const lwm_tensor4* v_shard, const int32_t* seg_q,
+                  const int32_t* seg_k, int64_t q_offset, int64_t k_offset, int32_t causal, float scale,
+                  const lwm_tensor4* o_acc, float* lse_acc, const lwm_tensor4* o_final, void* stream) {
+  int s;
+  if ((s = check_attention(q, k_shard, v_shard, seg_q, seg_k, q_offset, k_offset, causal))) return s;
+  if (q->dtype != LWM_BF16) return fail(LWM_ERR_UNSUPPORTED, "ring step is implemented for bf16 only");
+  if ((s = check_tensor(o_acc, "o_acc"))) return s;
+  if (o_acc->dtype != LWM_FP32) return fail(LWM_ERR_INVALID_ARG, "o_acc must be float32");
+  if (o_acc->B != q->B || o_acc->L != q->L || o_acc->H != q->H || o_acc->D != q->D)
+    return fail(LWM_ERR_INVALID_ARG, "o_acc shape must equal q's");
+  if (o_final) {
+    if ((s = check_tensor(o_final, "o_final")) || (s = check_same(q, o_final, "q", "o_final", true))) return s;
+  }
+  const bool empty = q->B == 0 || q->L == 0 || q->H == 0;
+  if (!empty && !lse_acc) return fail(LWM_ERR_INVALID_ARG, "lse_acc is NULL");
+  if (lse_acc && reinterpret_cast<uintptr_t>(lse_acc) % 4) return fail(LWM_ERR_INVALID_ARG, "lse_acc not 4-byte aligned");
+  float sc;
+  if ((s = check_scale(scale, q->D, &sc))) return s;
+  lwm::FwdParams p{};
+  p.q = q->ptr; p.k = k_shard->ptr; p.v = v_shard->ptr;
+  p.sq = strides(q); p.sk = strides(k_shard); p.sv = strides(v_shard);
+  p.B = (int)q->B; p.H = (int)q->H; p.Lq = (int)q->L; p.Lk = (int)k_shard->L;
+  p.seg_q = seg_q; p.seg_k = seg_k;
+  p.q_offset = q_offset; p.k_offset = k_offset; p.causal = causal;
+  p.scale_log2 = sc * 1.4426950408889634f;
+  p.o = o_final ? o_final->ptr : nullptr;
+  if (o_final) p.so = strides(o_final);
+  p.lse = nullptr;
+  p.o_acc = static_cast<float*>(o_acc->ptr);
+  p.soa = strides(o_acc);
+  p.lse_acc = lse_acc;
+  p.mode = 1;
+  return hip_status(lwm::launch_attn_fwd(p, true, static_cast<hipStream_t>(stream)), "ring step launch");
+}
+
+}  // extern "C"

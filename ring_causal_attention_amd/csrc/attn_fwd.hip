@@ -1,0 +1,625 @@
+// Blockwise causal attention forward and ring step for gfx950.
+//
+// Method: blockwise self-attention over query and key chunks ("LWM：突破 100 万 Token 的开源大模型",
+// section 配置参数) with the exact online softmax, causal ("Inside Large World Model ...", section
+// "Core Architecture") and packing ("LWM：突破 100 万 Token 的开源大模型", section 概述 (b)) masks,
+// and the ring step that folds one KV shard into a running (O, lse) state ("开源巨兽LWM：如何用
+// RingAttention撬动百万Token多模态世界", section 3.1).
+//
+// Design (bf16 path):
+//  * A workgroup of 4 waves owns BM = 4 * 32 * QB query rows of one (batch, head); each wave owns
+//    32 * QB rows whose Q fragments stay in registers for the whole pass.
+//  * K and V tiles of 64 keys stream HBM -> registers -> LDS, double-buffered: the global loads of
+//    tile j+1 are in flight while tile j is computed.  K is stored row-major with a 16-byte-chunk
+//    XOR swizzle; V is stored transposed (feature-major) with the keys of each 16-key group
+//    permuted to match the MFMA accumulator layout, so P never leaves registers.
+//  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: each lane then
+//    holds one query column, so the row max / row sum are in-lane plus a single exchange between
+//    the two wave halves, and the O^T accumulator's rescale is a per-lane multiply.
+//  * P^T (rounded to bf16) is the B operand of O^T += V^T P^T straight from the accumulator
+//    registers.  l sums the bf16-rounded p (v_dot2_f32_bf16), so O is a true convex combination.
+//  * The running max is only raised when a row's new max exceeds it by more than 2^8 (log2
+//    domain); in between p <= 256, which is exact in fp32 and keeps rescales rare.
+//  * Tiles wholly outside the causal / segment range are never visited; the mask is evaluated
+//    only on tiles that straddle a boundary or the ragged end.
+//  * Workgroups are numbered longest-first, and when B*H is a multiple of 8 the (batch, head)
+//    pairs are dealt to the 8 XCDs so the query tiles sharing one head's K/V run on one L2.
+#include <float.h>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace lwm {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * kWave;
+constexpr int BN = 64;  // keys per tile (bf16 path)
+constexpr int D = kHeadDim;
+constexpr float kRescaleSlack = 8.0f;  // log2 units: p <= 2^8 between rescales
+
+struct SmemBf16 {
+  u32x4 k[2][BN * 16];        // [stage][key][16 chunks], chunk c of key r at r*16 + (c ^ (r & 7))
+  u32x4 vt[2][D * (BN / 8)];  // [stage][feature][8 chunks], swizzled by vt_swz(d)
+  int32_t seg[2][BN];
+};
+static_assert(sizeof(SmemBf16) <= 80 * 1024, "two workgroups per CU must fit in LDS");
+
+__device__ __forceinline__ int vt_swz(int d) { return (d & 7) ^ ((d >> 3) & 7); }
+
+// Position of key offset o (0..15) inside its 16-key group in the transposed V tile: the
+// accumulator rows a lane half owns ({0..3, 8..11} or {4..7, 12..15}) become contiguous.
+__device__ __forceinline__ int group_pos(int o) { return ((o >> 2) & 1) * 8 + (o >> 3) * 4 + (o & 3); }
+
+// Grid position -> (batch*head, query tile).  Longest causal tiles first; with (B*H) % 8 == 0
+// consecutive dispatch slots of one XCD (block ids congruent mod 8) walk one head's tiles.
+__device__ __forceinline__ void map_block(int bid, int nqt, int BH, int& bh, int& qt) {
+  if ((BH & 7) == 0) {
+    const int xcd = bid & 7, slot = bid >> 3;
+    bh = (slot / nqt) * 8 + xcd;
+    qt = nqt - 1 - (slot % nqt);
+  } else {
+    bh = bid / nqt;
+    qt = nqt - 1 - (bid % nqt);
+  }
+}
+
+// Key range [kbeg, kend) that can be visible to query rows [r0, r1] (inclusive).
+__device__ inline void key_range(const FwdParams& p, int b, int r0, int r1, int& kbeg, int& kend) {
+  kbeg = 0;
+  kend = p.Lk;
+  if (p.causal) {
+    const int64_t lim = p.q_offset + r1 - p.k_offset + 1;
+    kend = (int)max<int64_t>(0, min<int64_t>(kend, lim));
+  }
+  if (p.seg_q) {
+    const int32_t* sk = p.seg_k + (int64_t)b * p.Lk;
+    const int32_t s0 = p.seg_q[(int64_t)b * p.Lq + r0];
+    const int32_t s1 = p.seg_q[(int64_t)b * p.Lq + r1];
+    kbeg = max(kbeg, wave_lower_bound(sk, p.Lk, s0));
+    kend = min(kend, s1 == INT32_MAX ? p.Lk : wave_lower_bound(sk, p.Lk, s1 + 1));
+  }
+}
+
+// ---------------------------------------------------------------------------- epilogue staging
+// Rows of a wave's O^T accumulator (lane = query column) are transposed through LDS so that
+// global stores are whole 16-byte chunks of contiguous rows.
+template <int QB>
+__device__ inline void store_rows_bf16(uint8_t* stage, const f32x16 (&acc)[4], const float inv,
+                                       uint16_t* gbase, int64_t row_stride, int rows_valid) {
+  // stage: 32 rows x 16 chunks (16 B) per wave, chunk c of row r at r*16 + (c ^ (r & 15))
+  const int lane = threadIdx.x & 63, c32 = lane & 31, h32 = lane >> 5;
+  u32x2* st2 = reinterpret_cast<u32x2*>(stage);
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int chunk = db * 4 + g;  // features db*32 + g*8 .. +7; this half holds 4 of them
+      u32x2 w;
+      w.x = pack_bf16x2(acc[db][g * 4 + 0] * inv, acc[db][g * 4 + 1] * inv);
+      w.y = pack_bf16x2(acc[db][g * 4 + 2] * inv, acc[db][g * 4 + 3] * inv);
+      st2[(c32 * 16 + (chunk ^ (c32 & 15))) * 2 + h32] = w;
+    }
+  __syncthreads();
+  const u32x4* st4 = reinterpret_cast<const u32x4*>(stage);
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int r = it * 4 + (lane >> 4), c = lane & 15;
+    if (r < rows_valid)
+      *reinterpret_cast<u32x4*>(gbase + r * row_stride + c * 8) = st4[r * 16 + (c ^ (r & 15))];
+  }
+  __syncthreads();
+}
+
+__device__ inline void store_rows_f32(uint8_t* stage, const f32x16 (&acc)[4], const float inv,
+                                      float* gbase, int64_t row_stride, int rows_valid) {
+  // stage: 32 rows x 32 chunks (16 B), chunk c of row r at r*32 + (c ^ (r & 31))
+  const int lane = threadIdx.x & 63, c32 = lane & 31, h32 = lane >> 5;
+  f32x4* st = reinterpret_cast<f32x4*>(stage);
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int chunk = db * 8 + g * 2 + h32;
+      f32x4 w;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[j] = acc[db][g * 4 + j] * inv;
+      st[c32 * 32 + (chunk ^ (c32 & 31))] = w;
+    }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < 16; ++it) {
+    const int r = it * 2 + (lane >> 5), c = lane & 31;
+    if (r < rows_valid) *reinterpret_cast<f32x4*>(gbase + r * row_stride + c * 4) = st[r * 32 + (c ^ (r & 31))];
+  }
+  __syncthreads();
+}
+
+__device__ inline void load_rows_f32(uint8_t* stage, f32x16 (&acc)[4], const float* gbase,
+                                     int64_t row_stride, int rows_valid) {
+  const int lane = threadIdx.x & 63, c32 = lane & 31, h32 = lane >> 5;
+  f32x4* st = reinterpret_cast<f32x4*>(stage);
+#pragma unroll
+  for (int it = 0; it < 16; ++it) {
+    const int r = it * 2 + (lane >> 5), c = lane & 31;
+    f32x4 w = {0.f, 0.f, 0.f, 0.f};
+    if (r < rows_valid) w = *reinterpret_cast<const f32x4*>(gbase + r * row_stride + c * 4);
+    st[r * 32 + (c ^ (r & 31))] = w;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int chunk = db * 8 + g * 2 + h32;
+      const f32x4 w = st[c32 * 32 + (chunk ^ (c32 & 31))];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[db][g * 4 + j] = w[j];
+    }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------- bf16 kernel
+template <int QB>
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdParams p) {
+  constexpr int MW = 32 * QB;
+  constexpr int BM = kWaves * MW;
+  __shared__ SmemBf16 sm;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int c32 = lane & 31, h32 = lane >> 5;
+  const int nqt = (p.Lq + BM - 1) / BM;
+  int bh, qt;
+  map_block(blockIdx.x, nqt, p.B * p.H, bh, qt);
+  const int b = bh / p.H, hh = bh - b * p.H;
+  const int q0 = qt * BM;
+  const int qlast = min(q0 + BM, p.Lq) - 1;
+
+  int kbeg, kend;
+  key_range(p, b, q0, qlast, kbeg, kend);
+  const int t_begin = kbeg / BN;
+  const int ntiles = (kend > kbeg) ? (kend + BN - 1) / BN - t_begin : 0;
+
+  // this wave's rows and their visibility bounds
+  const int wr0 = q0 + w * MW;
+  const int wr1 = min(wr0 + MW, p.Lq) - 1;  // may be < wr0 for a ragged last tile
+  const bool wave_rows = wr1 >= wr0;
+  const bool segs = p.seg_q != nullptr;
+  int32_t wseg0 = 0, wseg1 = 0;
+  if (segs && wave_rows) {
+    wseg0 = p.seg_q[(int64_t)b * p.Lq + wr0];
+    wseg1 = p.seg_q[(int64_t)b * p.Lq + wr1];
+  }
+
+  const uint16_t* __restrict__ qg = static_cast<const uint16_t*>(p.q) + b * p.sq.b + hh * p.sq.h;
+  const uint16_t* __restrict__ kg = static_cast<const uint16_t*>(p.k) + b * p.sk.b + hh * p.sk.h;
+  const uint16_t* __restrict__ vg = static_cast<const uint16_t*>(p.v) + b * p.sv.b + hh * p.sv.h;
+
+  int qrow[QB];
+  int64_t gq[QB];
+  int32_t myseg[QB];
+  bf16x8 qreg[QB][8];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    qrow[qb] = wr0 + qb * 32 + c32;
+    gq[qb] = p.q_offset + qrow[qb];
+    myseg[qb] = segs ? p.seg_q[(int64_t)b * p.Lq + min(qrow[qb], p.Lq - 1)] : 0;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (qrow[qb] < p.Lq) v = *reinterpret_cast<const u32x4*>(qg + qrow[qb] * p.sq.l + s * 16 + h32 * 8);
+      qreg[qb][s] = as_bf16x8(v);
+    }
+  }
+
+  // running state: O^T accumulators, row max m (log2-scaled), partial row sum l (this half's keys)
+  f32x16 acc[QB][4];
+  float m[QB], l[QB], m_init[QB];
+  const bool ring = p.mode == 1;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[qb][db][i] = 0.f;
+    m[qb] = -INFINITY;
+    l[qb] = 0.f;
+  }
+  uint8_t* stage_w = reinterpret_cast<uint8_t*>(&sm) + w * (32 * D * 4);
+  if (ring && ntiles > 0) {
+    float* oag = p.o_acc + b * p.soa.b + hh * p.soa.h;
+    const float* lag = p.lse_acc + ((int64_t)b * p.H + hh) * p.Lq;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int r0 = wr0 + qb * 32;
+      load_rows_f32(stage_w, acc[qb], oag + r0 * p.soa.l, p.soa.l, max(0, min(32, p.Lq - r0)));
+      const float ls = qrow[qb] < p.Lq ? lag[qrow[qb]] : -INFINITY;
+      m[qb] = ls * kLog2e;
+      l[qb] = h32 == 0 ? 1.f : 0.f;
+    }
+  }
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) m_init[qb] = m[qb];
+
+  // ---- register-staged K/V tile loader
+  u32x4 kst[4], vst[4];
+  int32_t segst = -1;
+  const int ld_key = tid >> 4, ld_c = tid & 15;  // K: 4 passes of 16 keys x 16 chunks
+  const int ld_kq = tid >> 4, ld_dg = tid & 15;  // V: key quad x feature chunk
+  auto gload = [&](int tile) {
+    const int k0 = tile * BN;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = k0 + r * 16 + ld_key;
+      kst[r] = (key < p.Lk) ? *reinterpret_cast<const u32x4*>(kg + key * p.sk.l + ld_c * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = k0 + 4 * ld_kq + r;
+      vst[r] = (key < p.Lk) ? *reinterpret_cast<const u32x4*>(vg + key * p.sv.l + ld_dg * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (segs && tid < BN) segst = (k0 + tid < p.Lk) ? p.seg_k[(int64_t)b * p.Lk + k0 + tid] : -1;
+  };
+  auto swrite = [&](int st) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = r * 16 + ld_key;
+      sm.k[st][key * 16 + (ld_c ^ (key & 7))] = kst[r];
+    }
+    // V: transpose 4 keys x 8 features into 8 features x 4 keys (8 bytes each)
+    const int quad = ld_kq & 3, grp = ld_kq >> 2;
+    const int chunk = grp * 2 + (quad & 1);
+    const int sub = quad >> 1;
+#pragma unroll
+    for (int jd = 0; jd < 8; ++jd) {
+      const int d = ld_dg * 8 + jd;
+      const int word = jd >> 1;
+      uint32_t w0, w1;
+      if (jd & 1) {
+        w0 = (vst[0][word] >> 16) | (vst[1][word] & 0xffff0000u);
+        w1 = (vst[2][word] >> 16) | (vst[3][word] & 0xffff0000u);
+      } else {
+        w0 = (vst[0][word] & 0xffffu) | (vst[1][word] << 16);
+        w1 = (vst[2][word] & 0xffffu) | (vst[3][word] << 16);
+      }
+      u32x2* dst = reinterpret_cast<u32x2*>(&sm.vt[st][d * 8 + (chunk ^ vt_swz(d))]);
+      dst[sub] = u32x2{w0, w1};
+    }
+    if (segs && tid < BN) sm.seg[st][tid] = segst;
+  };
+
+  if (ntiles > 0) {
+    gload(t_begin);
+    swrite(0);
+    __syncthreads();
+  }
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int st = it & 1;
+    const int k0 = (t_begin + it) * BN;
+    if (it + 1 < ntiles) gload(t_begin + it + 1);
+
+    // does this wave see any key of the tile, and does it need the element mask?
+    bool active = wave_rows;
+    bool need_mask = (k0 + BN > p.Lk) || (k0 < kbeg) || (k0 + BN > kend);
+    if (p.causal) {
+      active = active && (p.k_offset + k0 <= p.q_offset + wr1);
+      need_mask = need_mask || (p.k_offset + k0 + BN - 1 > p.q_offset + wr0);
+    }
+    if (segs) {
+      const int32_t ts0 = sm.seg[st][0], ts1 = sm.seg[st][min(BN, p.Lk - k0) - 1];
+      active = active && !(ts1 < wseg0 || ts0 > wseg1);
+      need_mask = need_mask || !(ts0 == ts1 && wseg0 == wseg1 && ts0 == wseg0);
+    }
+
+    if (active) {
+      // ---- S^T = K Q^T: [2 key blocks][QB query blocks] of 32x32
+      f32x16 s[2][QB];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) s[kb][qb][i] = 0.f;
+#pragma unroll
+      for (int sd = 0; sd < 8; ++sd) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int key = kb * 32 + c32;
+          const int chunk = 2 * sd + h32;
+          const bf16x8 a = as_bf16x8(sm.k[st][key * 16 + (chunk ^ (key & 7))]);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma_32x32x16(a, qreg[qb][sd], s[kb][qb]);
+        }
+      }
+
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int kl = kb * 32 + acc_row(i, h32);
+            const int key = k0 + kl;
+            const bool in_range = key < p.Lk;
+            const int32_t ks = segs ? sm.seg[st][kl] : 0;
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+              bool vis = in_range;
+              if (p.causal) vis = vis && (p.k_offset + key <= gq[qb]);
+              if (segs) vis = vis && (ks == myseg[qb]);
+              if (!vis) s[kb][qb][i] = -INFINITY;
+            }
+          }
+      }
+
+      // ---- online softmax (log2 domain), lazily rescaled
+      float mx[QB];
+      bool need_rescale = false;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float v = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) v = fmaxf(v, s[kb][qb][i]);
+        v = fmaxf(v, swap_halves(v));
+        mx[qb] = v * p.scale_log2;
+        need_rescale = need_rescale || (mx[qb] > m[qb] + kRescaleSlack);
+      }
+      if (__any(need_rescale)) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const float mnew = fmaxf(m[qb], mx[qb]);
+          const float alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(m[qb] - mnew);
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[qb][db][i] *= alpha;
+          l[qb] *= alpha;
+          m[qb] = mnew;
+        }
+      }
+
+      // p = exp2(s * scale_log2 - m), rounded to bf16; l += sum of the rounded values
+      bf16x8 pb[2][2][QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float moff = (m[qb] == -INFINITY) ? 0.f : m[qb];
+        float lsum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            u32x4 packed;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float e0 = fast_exp2(__builtin_fmaf(s[kb][qb][u * 8 + 2 * j], p.scale_log2, -moff));
+              const float e1 = fast_exp2(__builtin_fmaf(s[kb][qb][u * 8 + 2 * j + 1], p.scale_log2, -moff));
+              packed[j] = pack_bf16x2(e0, e1);
+              lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed[j]),
+                                                     bf16x2{(__bf16)1.0f, (__bf16)1.0f}, lsum, false);
+            }
+            pb[kb][u][qb] = as_bf16x8(packed);
+          }
+        l[qb] += lsum;
+      }
+
+      // ---- O^T += V^T P^T
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int g = kb * 2 + u;
+#pragma unroll
+          for (int db = 0; db < 4; ++db) {
+            const int d = db * 32 + c32;
+            const int chunk = g * 2 + h32;
+            const bf16x8 a = as_bf16x8(sm.vt[st][d * 8 + (chunk ^ vt_swz(d))]);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma_32x32x16(a, pb[kb][u][qb], acc[qb][db]);
+          }
+        }
+    }
+
+    if (it + 1 < ntiles) swrite(st ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = acc / l, lse = (m + log2 l) ln 2
+  uint16_t* og = static_cast<uint16_t*>(p.o);
+  float* lse_row = p.lse ? p.lse + ((int64_t)b * p.H + hh) * p.Lq : nullptr;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int r0 = wr0 + qb * 32;
+    const int rows_valid = max(0, min(32, p.Lq - r0));
+    const float lt = l[qb] + swap_halves(l[qb]);
+    const bool any = (lt > 0.f) && (m[qb] != -INFINITY);
+    const float inv = any ? 1.f / lt : 0.f;
+    const float lse = any ? (m[qb] + log2f(lt)) * kLn2 : -INFINITY;
+    if (!ring) {
+      if (og) store_rows_bf16<QB>(stage_w, acc[qb], inv, og + b * p.so.b + hh * p.so.h + r0 * p.so.l, p.so.l, rows_valid);
+      if (lse_row && h32 == 0 && qrow[qb] < p.Lq) lse_row[qrow[qb]] = lse;
+    } else {
+      float* lag = p.lse_acc + ((int64_t)b * p.H + hh) * p.Lq;
+      float* oag = p.o_acc + b * p.soa.b + hh * p.soa.h + r0 * p.soa.l;
+      uint16_t* ofg = og ? og + b * p.so.b + hh * p.so.h + r0 * p.so.l : nullptr;
+      if (ntiles > 0) {
+        // a row that saw nothing new keeps its state bit for bit
+        const bool untouched = (m[qb] == m_init[qb]) && (lt == 1.f);
+        const float sc = untouched ? 1.f : inv;
+        store_rows_f32(stage_w, acc[qb], sc, oag, p.soa.l, rows_valid);
+        if (h32 == 0 && qrow[qb] < p.Lq && !untouched) lag[qrow[qb]] = lse;
+        if (ofg) store_rows_bf16<QB>(stage_w, acc[qb], sc, ofg, p.so.l, rows_valid);
+      } else if (ofg) {
+        // nothing visible in this shard for the whole tile: the bf16 copy is the state itself
+        f32x16 tmp[4];
+        load_rows_f32(stage_w, tmp, oag, p.soa.l, rows_valid);
+        store_rows_bf16<QB>(stage_w, tmp, 1.f, ofg, p.so.l, rows_valid);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------- fp32 kernel
+// Same structure on v_mfma_f32_32x32x2_f32 (float32 everywhere, no rounding of P); 32-key
+// tiles, one query block per wave, fresh state only.
+constexpr int BN32 = 32;
+constexpr int kPad32 = D + 1;  // LDS row pitch (floats): rows land on distinct banks
+
+struct SmemF32 {
+  float k[2][BN32 * kPad32];
+  float v[2][BN32 * kPad32];
+  int32_t seg[2][BN32];
+};
+
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_f32_kernel(FwdParams p) {
+  constexpr int MW = 32, BM = kWaves * MW;
+  __shared__ SmemF32 sm;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int c32 = lane & 31, h32 = lane >> 5;
+  const int nqt = (p.Lq + BM - 1) / BM;
+  int bh, qt;
+  map_block(blockIdx.x, nqt, p.B * p.H, bh, qt);
+  const int b = bh / p.H, hh = bh - b * p.H;
+  const int q0 = qt * BM;
+  const int qlast = min(q0 + BM, p.Lq) - 1;
+  int kbeg, kend;
+  key_range(p, b, q0, qlast, kbeg, kend);
+  const int t_begin = kbeg / BN32;
+  const int ntiles = (kend > kbeg) ? (kend + BN32 - 1) / BN32 - t_begin : 0;
+  const bool segs = p.seg_q != nullptr;
+
+  const float* __restrict__ qg = static_cast<const float*>(p.q) + b * p.sq.b + hh * p.sq.h;
+  const float* __restrict__ kg = static_cast<const float*>(p.k) + b * p.sk.b + hh * p.sk.h;
+  const float* __restrict__ vg = static_cast<const float*>(p.v) + b * p.sv.b + hh * p.sv.h;
+
+  const int qrow = q0 + w * MW + c32;
+  const int64_t gq = p.q_offset + qrow;
+  const int32_t myseg = segs ? p.seg_q[(int64_t)b * p.Lq + min(qrow, p.Lq - 1)] : 0;
+  float qreg[64];  // feature 2*s + h32
+#pragma unroll
+  for (int c = 0; c < 32; ++c) {
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    if (qrow < p.Lq) v = *reinterpret_cast<const f32x4*>(qg + qrow * p.sq.l + c * 4);
+    qreg[2 * c] = v[h32];
+    qreg[2 * c + 1] = v[2 + h32];
+  }
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+  float m = -INFINITY, l = 0.f;
+
+  f32x4 kst[4], vst[4];
+  int32_t segst = -1;
+  auto gload = [&](int tile) {
+    const int k0 = tile * BN32;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int e = r * kThreads + tid;  // 32 keys x 32 chunks of 4 floats
+      const int key = k0 + (e >> 5), c = e & 31;
+      kst[r] = key < p.Lk ? *reinterpret_cast<const f32x4*>(kg + key * p.sk.l + c * 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+      vst[r] = key < p.Lk ? *reinterpret_cast<const f32x4*>(vg + key * p.sv.l + c * 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    if (segs && tid < BN32) segst = (k0 + tid < p.Lk) ? p.seg_k[(int64_t)b * p.Lk + k0 + tid] : -1;
+  };
+  auto swrite = [&](int st) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int e = r * kThreads + tid;
+      const int key = e >> 5, c = e & 31;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sm.k[st][key * kPad32 + c * 4 + j] = kst[r][j];
+        sm.v[st][key * kPad32 + c * 4 + j] = vst[r][j];
+      }
+    }
+    if (segs && tid < BN32) sm.seg[st][tid] = segst;
+  };
+
+  if (ntiles > 0) {
+    gload(t_begin);
+    swrite(0);
+    __syncthreads();
+  }
+  const int wr0 = q0 + w * MW, wr1 = min(wr0 + MW, p.Lq) - 1;
+  for (int it = 0; it < ntiles; ++it) {
+    const int st = it & 1;
+    const int k0 = (t_begin + it) * BN32;
+    if (it + 1 < ntiles) gload(t_begin + it + 1);
+    bool active = wr1 >= wr0;
+    if (p.causal) active = active && (p.k_offset + k0 <= p.q_offset + wr1);
+    if (active) {
+      f32x16 s;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = 0.f;
+#pragma unroll
+      for (int sd = 0; sd < 64; ++sd) s = mfma_32x32x2_f32(sm.k[st][c32 * kPad32 + 2 * sd + h32], qreg[sd], s);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kl = acc_row(i, h32);
+        const int key = k0 + kl;
+        bool vis = key < p.Lk && key >= kbeg && key < kend;
+        if (p.causal) vis = vis && (p.k_offset + key <= gq);
+        if (segs) vis = vis && (sm.seg[st][kl] == myseg);
+        if (!vis) s[i] = -INFINITY;
+      }
+      float v = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v = fmaxf(v, s[i]);
+      v = fmaxf(v, swap_halves(v)) * p.scale_log2;
+      if (__any(v > m)) {
+        const float mnew = fmaxf(m, v);
+        const float alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(m - mnew);
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+        l *= alpha;
+        m = mnew;
+      }
+      const float moff = (m == -INFINITY) ? 0.f : m;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s[i] = exp2f(__builtin_fmaf(s[i], p.scale_log2, -moff));
+        l += s[i];
+      }
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int t = 0; t < 16; ++t)
+          acc[db] = mfma_32x32x2_f32(sm.v[st][acc_row(t, h32) * kPad32 + db * 32 + c32], s[t], acc[db]);
+    }
+    if (it + 1 < ntiles) swrite(st ^ 1);
+    __syncthreads();
+  }
+
+  const float lt = l + swap_halves(l);
+  const bool any = (lt > 0.f) && (m != -INFINITY);
+  const float inv = any ? 1.f / lt : 0.f;
+  const float lse = any ? (m + log2f(lt)) * kLn2 : -INFINITY;
+  uint8_t* stage_w = reinterpret_cast<uint8_t*>(&sm) + w * (32 * D * 4);
+  float* og = static_cast<float*>(p.o) + b * p.so.b + hh * p.so.h + wr0 * p.so.l;
+  store_rows_f32(stage_w, acc, inv, og, p.so.l, max(0, min(32, p.Lq - wr0)));
+  if (p.lse && h32 == 0 && qrow < p.Lq) p.lse[((int64_t)b * p.H + hh) * p.Lq + qrow] = lse;
+}
+static_assert(sizeof(SmemF32) >= kWaves * 32 * D * 4, "epilogue staging must fit");
+
+}  // namespace
+
+hipError_t launch_attn_fwd(const FwdParams& p, bool bf16, hipStream_t stream) {
+  if (p.Lq == 0 || p.B == 0 || p.H == 0) return hipSuccess;
+  if (bf16) {
+    constexpr int QB = 1, BM = kWaves * 32 * QB;
+    const int nqt = (p.Lq + BM - 1) / BM;
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel<QB>, dim3(nqt * p.B * p.H), dim3(kThreads), 0, stream, p);
+  } else {
+    const int nqt = (p.Lq + 127) / 128;
+    hipLaunchKernelGGL(attn_fwd_f32_kernel, dim3(nqt * p.B * p.H), dim3(kThreads), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace lwm

@@ -1,0 +1,79 @@
+// Kernel parameter blocks and launchers (internal to the library; the public surface is the
+// C ABI in include/lwm_attn.h).  Strides are in elements; the feature stride is 1.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lwm {
+
+constexpr int kMaxRopeHalf = 128;
+constexpr int kHeadDim = 128;  // the attention kernels are written for D = 128
+
+struct RopeParams {
+  const void* x;
+  void* y;
+  const int32_t* pos;
+  const int32_t* seg;
+  int64_t pos_offset;
+  int B, L, H, D;
+  int64_t xsB, xsL, xsH;
+  int64_t ysB, ysL, ysH;
+  int layout;   // 0: (i, i + D/2), 1: (2i, 2i + 1)
+  int inverse;  // rotate by -angle
+  double inv_freq[kMaxRopeHalf];
+};
+
+struct Strides {
+  int64_t b, l, h;
+};
+
+// Forward / ring-step attention.  mode 0: fresh state, writes o (+ lse).  mode 1: ring step,
+// state read from and written back to o_acc / lse_acc, o optional (bf16 copy of the result).
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  Strides sq, sk, sv;
+  int B, H, Lq, Lk;
+  const int32_t* seg_q;
+  const int32_t* seg_k;
+  int64_t q_offset, k_offset;
+  int causal;
+  float scale_log2;  // scale * log2(e)
+  void* o;
+  Strides so;
+  float* lse;
+  float* o_acc;
+  Strides soa;
+  float* lse_acc;
+  int mode;
+};
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  Strides sq, sk, sv, so, sdo;
+  const float* lse;
+  float* delta;  // workspace [B, H, Lq]: rowsum(dout * o)
+  int B, H, Lq, Lk;
+  const int32_t* seg_q;
+  const int32_t* seg_k;
+  int64_t q_offset, k_offset;
+  int causal;
+  float scale;
+  float scale_log2;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  Strides sdq, sdk, sdv;
+};
+
+hipError_t launch_rope(const RopeParams& p, bool bf16, hipStream_t stream);
+hipError_t launch_attn_fwd(const FwdParams& p, bool bf16, hipStream_t stream);
+hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t stream);
+
+}  // namespace lwm

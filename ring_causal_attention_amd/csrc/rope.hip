@@ -1,0 +1,160 @@
+// RoPE with theta scaled to the context length ("[论文解读] World Model on Million-Length Video
+// And Language With Blockwise RingAttention", section 提出的方法), applied to a [B, L, H, D]
+// tensor in place or out of place, forward or inverse.
+//
+// HBM-bound: every element is read and written once.  A workgroup owns kTok consecutive tokens
+// of one batch row.  It first forms the kTok x D/2 angles once (double precision: position times
+// inv_freq, reduced modulo 2*pi) and their sine/cosine (single precision) in LDS, then streams
+// all H heads of those tokens with 16-byte vector loads and stores, so the trigonometry is shared
+// by every head instead of being repeated per element.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace lwm {
+namespace {
+
+constexpr int kTok = 4;
+constexpr int kThreads = 256;
+
+// Index of the first token of t's segment: first p with seg[p] == seg[t], ids non-decreasing.
+__device__ int segment_start(const int32_t* __restrict__ seg, int t) {
+  const int32_t v = seg[t];
+  int lo = 0, hi = t;  // answer in [lo, hi]
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (seg[mid] < v) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+template <typename T>
+struct Vec;
+template <>
+struct Vec<uint16_t> {  // bf16: 8 elements per 16 bytes
+  static constexpr int N = 8;
+  __device__ static void load(const uint16_t* p, float (&x)[N]) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = bf16_lo(w[j]);
+      x[2 * j + 1] = bf16_hi(w[j]);
+    }
+  }
+  __device__ static void store(uint16_t* p, const float (&x)[N]) {
+    u32x4 w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = pack_bf16x2(x[2 * j], x[2 * j + 1]);
+    *reinterpret_cast<u32x4*>(p) = w;
+  }
+};
+template <>
+struct Vec<float> {  // fp32: 4 elements per 16 bytes
+  static constexpr int N = 4;
+  __device__ static void load(const float* p, float (&x)[N]) {
+    const f32x4 w = *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = w[j];
+  }
+  __device__ static void store(float* p, const float (&x)[N]) {
+    f32x4 w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = x[j];
+    *reinterpret_cast<f32x4*>(p) = w;
+  }
+};
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void rope_kernel(RopeParams p) {
+  __shared__ float2 cs[kTok][kMaxRopeHalf];  // (cos, sin) per token and pair
+  const int b = blockIdx.y;
+  const int t0 = blockIdx.x * kTok;
+  const int half = p.D / 2;
+  const int ntok = min(kTok, p.L - t0);
+
+  // ---- phase 1: angles (double), sin/cos (float) for kTok tokens x D/2 pairs
+  const double two_pi_hi = 6.283185307179586;          // nearest double to 2*pi
+  const double two_pi_lo = 2.4492935982947064e-16;     // 2*pi - two_pi_hi
+  const double inv_two_pi = 0.15915494309189535;
+  for (int e = threadIdx.x; e < ntok * half; e += kThreads) {
+    const int tt = e / half, i = e - tt * half;
+    const int t = t0 + tt;
+    int64_t pos;
+    if (p.pos) pos = p.pos[(int64_t)b * p.L + t];
+    else if (p.seg) pos = t - segment_start(p.seg + (int64_t)b * p.L, t);
+    else pos = t;
+    pos += p.pos_offset;
+    const double ang = (double)pos * p.inv_freq[i];
+    const double k = rint(ang * inv_two_pi);
+    double r = fma(-k, two_pi_hi, ang);
+    r = fma(-k, two_pi_lo, r);
+    float s, c;
+    sincosf((float)r, &s, &c);
+    cs[tt][i] = make_float2(c, p.inverse ? -s : s);
+  }
+  __syncthreads();
+
+  // ---- phase 2: rotate every head of the kTok tokens, 16 bytes at a time
+  constexpr int N = Vec<T>::N;
+  const T* __restrict__ x = static_cast<const T*>(p.x);
+  T* __restrict__ y = static_cast<T*>(p.y);
+  if (p.layout == 0) {
+    // pairs (i, i + D/2): chunk c of the first half with chunk c of the second half
+    const int nchunk = half / N;
+    const int items = ntok * p.H * nchunk;
+    for (int e = threadIdx.x; e < items; e += kThreads) {
+      const int c = e % nchunk;
+      const int rest = e / nchunk;
+      const int h = rest % p.H, tt = rest / p.H;
+      const int64_t t = t0 + tt;
+      const T* xs = x + b * p.xsB + t * p.xsL + h * p.xsH + c * N;
+      T* ys = y + b * p.ysB + t * p.ysL + h * p.ysH + c * N;
+      float a[N], bb[N];
+      Vec<T>::load(xs, a);
+      Vec<T>::load(xs + half, bb);
+#pragma unroll
+      for (int j = 0; j < N; ++j) {
+        const float2 r = cs[tt][c * N + j];
+        const float ra = a[j] * r.x - bb[j] * r.y;
+        const float rb = a[j] * r.y + bb[j] * r.x;
+        a[j] = ra;
+        bb[j] = rb;
+      }
+      Vec<T>::store(ys, a);
+      Vec<T>::store(ys + half, bb);
+    }
+  } else {
+    // pairs (2i, 2i + 1): each 16-byte chunk holds N/2 whole pairs
+    const int nchunk = p.D / N;
+    const int items = ntok * p.H * nchunk;
+    for (int e = threadIdx.x; e < items; e += kThreads) {
+      const int c = e % nchunk;
+      const int rest = e / nchunk;
+      const int h = rest % p.H, tt = rest / p.H;
+      const int64_t t = t0 + tt;
+      const T* xs = x + b * p.xsB + t * p.xsL + h * p.xsH + c * N;
+      T* ys = y + b * p.ysB + t * p.ysL + h * p.ysH + c * N;
+      float a[N];
+      Vec<T>::load(xs, a);
+#pragma unroll
+      for (int j = 0; j < N / 2; ++j) {
+        const float2 r = cs[tt][c * (N / 2) + j];
+        const float u = a[2 * j], w = a[2 * j + 1];
+        a[2 * j] = u * r.x - w * r.y;
+        a[2 * j + 1] = u * r.y + w * r.x;
+      }
+      Vec<T>::store(ys, a);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rope(const RopeParams& p, bool bf16, hipStream_t stream) {
+  if (p.L == 0 || p.B == 0 || p.H == 0) return hipSuccess;
+  dim3 grid((p.L + kTok - 1) / kTok, p.B);
+  if (bf16) hipLaunchKernelGGL(rope_kernel<uint16_t>, grid, dim3(kThreads), 0, stream, p);
+  else hipLaunchKernelGGL(rope_kernel<float>, grid, dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace lwm

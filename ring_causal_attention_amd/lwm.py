@@ -1,0 +1,165 @@
+"""ctypes binding of liblwm_attn.so with the C ABI's names (argument marshalling only).
+
+Each function takes torch tensors already on the GPU in the ``[B, L, H, D]`` layout (feature
+stride 1), passes their pointers, sizes and strides to the C entry point of the same name and
+enqueues the work on ``torch.cuda.current_stream()``.  Outputs that are not passed in are
+allocated with ``torch.empty``.  Nothing here computes any part of the method: if the library
+is missing or a call fails, a ``LwmError`` is raised; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("LWM_ATTN_LIB", os.path.join(_HERE, "liblwm_attn.so"))
+
+LWM_BF16, LWM_FP32 = 0, 1
+LAYOUTS = {"half": 0, "interleaved": 1}
+STATUS = {0: "LWM_OK", -1: "LWM_ERR_INVALID_ARG", -2: "LWM_ERR_UNSUPPORTED", -3: "LWM_ERR_WORKSPACE", -4: "LWM_ERR_HIP"}
+
+
+class LwmError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class Tensor4(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("B", ctypes.c_int64), ("L", ctypes.c_int64), ("H", ctypes.c_int64), ("D", ctypes.c_int64),
+                ("sB", ctypes.c_int64), ("sL", ctypes.c_int64), ("sH", ctypes.c_int64)]
+
+
+_lib = None
+EXPORTS = ["lwm_abi_version", "lwm_last_error", "lwm_rope_apply", "lwm_blockattn_fwd",
+           "lwm_blockattn_bwd_workspace_size", "lwm_blockattn_bwd", "lwm_ring_step"]
+
+
+def lib() -> ctypes.CDLL:
+    """Load the library once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m ring_causal_attention_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, F32, F64, VP = (ctypes.POINTER(Tensor4), ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                                 ctypes.c_double, ctypes.c_void_p)
+    L.lwm_abi_version.restype = ctypes.c_int
+    L.lwm_abi_version.argtypes = []
+    L.lwm_last_error.restype = ctypes.c_char_p
+    L.lwm_last_error.argtypes = []
+    L.lwm_rope_apply.restype = ctypes.c_int
+    L.lwm_rope_apply.argtypes = [P, P, VP, VP, I64, F64, I32, I32, VP]
+    L.lwm_blockattn_fwd.restype = ctypes.c_int
+    L.lwm_blockattn_fwd.argtypes = [P, P, P, VP, VP, I64, I64, I32, F32, P, VP, VP]
+    L.lwm_blockattn_bwd_workspace_size.restype = ctypes.c_size_t
+    L.lwm_blockattn_bwd_workspace_size.argtypes = [I64, I64, I64, I64, I64]
+    L.lwm_blockattn_bwd.restype = ctypes.c_int
+    L.lwm_blockattn_bwd.argtypes = [P, P, P, P, VP, P, VP, VP, I64, I64, I32, F32, P, P, P, VP, ctypes.c_size_t, VP]
+    L.lwm_ring_step.restype = ctypes.c_int
+    L.lwm_ring_step.argtypes = [P, P, P, VP, VP, I64, I64, I32, F32, P, VP, P, VP]
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != 0:
+        raise LwmError(status, lib().lwm_last_error().decode(errors="replace"))
+
+
+def tensor4(t: torch.Tensor | None) -> Tensor4 | None:
+    """Describe a [B, L, H, D] tensor (feature stride 1) for the ABI."""
+    if t is None:
+        return None
+    if t.dim() != 4:
+        raise ValueError(f"expected a [B, L, H, D] tensor, got shape {tuple(t.shape)}")
+    if t.dtype == torch.bfloat16:
+        dt = LWM_BF16
+    elif t.dtype == torch.float32:
+        dt = LWM_FP32
+    else:
+        raise ValueError(f"unsupported dtype {t.dtype}")
+    if t.shape[3] > 1 and t.stride(3) != 1:
+        raise ValueError("the feature dimension must be contiguous")
+    B, L, H, D = t.shape
+    return Tensor4(t.data_ptr(), dt, 0, B, L, H, D, t.stride(0), t.stride(1), t.stride(2))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _ref(s):
+    return None if s is None else ctypes.byref(s)
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _seg(s):
+    if s is None:
+        return None
+    if s.dtype != torch.int32 or not s.is_contiguous():
+        raise ValueError("segment ids / positions must be contiguous int32 [B, L]")
+    return s
+
+
+def lwm_abi_version() -> int:
+    return lib().lwm_abi_version()
+
+
+def lwm_rope_apply(x, y=None, pos=None, seg=None, pos_offset=0, theta=10000.0, layout="half", inverse=False):
+    """RoPE of x into y (default: a new tensor; pass y=x for in place).  Returns y."""
+    y = torch.empty_like(x) if y is None else y
+    _check(lib().lwm_rope_apply(_ref(tensor4(x)), _ref(tensor4(y)), _ptr(_seg(pos)), _ptr(_seg(seg)), int(pos_offset),
+                                float(theta), LAYOUTS[layout], int(bool(inverse)), _stream(x)))
+    return y
+
+
+def lwm_blockattn_fwd(q, k, v, seg_q=None, seg_k=None, q_offset=0, k_offset=0, causal=True, scale=0.0,
+                      o=None, lse=None, want_lse=True):
+    """Forward; returns (o, lse) with lse float32 [B, H, Lq] (None if want_lse is False)."""
+    B, Lq, H, _ = q.shape
+    o = torch.empty_like(q) if o is None else o
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
+    _check(lib().lwm_blockattn_fwd(_ref(tensor4(q)), _ref(tensor4(k)), _ref(tensor4(v)), _ptr(_seg(seg_q)),
+                                   _ptr(_seg(seg_k)), int(q_offset), int(k_offset), int(bool(causal)), float(scale),
+                                   _ref(tensor4(o)), _ptr(lse), _stream(q)))
+    return o, lse
+
+
+def lwm_blockattn_bwd_workspace_size(B, H, Lq, Lk, D) -> int:
+    return int(lib().lwm_blockattn_bwd_workspace_size(B, H, Lq, Lk, D))
+
+
+def lwm_blockattn_bwd(q, k, v, o, lse, dout, seg_q=None, seg_k=None, q_offset=0, k_offset=0, causal=True,
+                      scale=0.0, dq=None, dk=None, dv=None, workspace=None):
+    """Backward; returns (dq, dk, dv) w.r.t. the operands given (the rotated Q', K')."""
+    B, Lq, H, D = q.shape
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = lwm_blockattn_bwd_workspace_size(B, H, Lq, k.shape[1], D)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(lib().lwm_blockattn_bwd(_ref(tensor4(q)), _ref(tensor4(k)), _ref(tensor4(v)), _ref(tensor4(o)), _ptr(lse),
+                                   _ref(tensor4(dout)), _ptr(_seg(seg_q)), _ptr(_seg(seg_k)), int(q_offset),
+                                   int(k_offset), int(bool(causal)), float(scale), _ref(tensor4(dq)),
+                                   _ref(tensor4(dk)), _ref(tensor4(dv)), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(q)))
+    return dq, dk, dv
+
+
+def lwm_ring_step(q, k_shard, v_shard, o_acc, lse_acc, seg_q=None, seg_k=None, q_offset=0, k_offset=0,
+                  causal=True, scale=0.0, o_final=None):
+    """Fold one KV shard into (o_acc float32 [B, Lq, H, D], lse_acc float32 [B, H, Lq]) in place."""
+    _check(lib().lwm_ring_step(_ref(tensor4(q)), _ref(tensor4(k_shard)), _ref(tensor4(v_shard)), _ptr(_seg(seg_q)),
+                               _ptr(_seg(seg_k)), int(q_offset), int(k_offset), int(bool(causal)), float(scale),
+                               _ref(tensor4(o_acc)), _ptr(lse_acc), _ref(tensor4(o_final)), _stream(q)))
+    return o_acc, lse_acc

@@ -1,0 +1,105 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol, and rejects bad
+arguments with the documented status before touching the GPU (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from ring_causal_attention_amd import lwm
+
+pytestmark = pytest.mark.cpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lwm_attn.h")
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lwm_[a-z0-9_]+)\s*\(", text)))
+
+
+def _lib():
+    if not os.path.exists(lwm.LIB_PATH):
+        pytest.skip("library not built (run __graft_entry__.build())")
+    return lwm.lib()
+
+
+def test_exports_every_declared_symbol():
+    L = _lib()
+    names = declared_functions()
+    assert set(names) == set(lwm.EXPORTS), names
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.lwm_abi_version() == 1
+    assert L.lwm_last_error() == b""
+
+
+def t4(ptr=16, dtype=0, B=1, L=8, H=2, D=128, sB=None, sL=None, sH=None):
+    sH = D if sH is None else sH
+    sL = H * D if sL is None else sL
+    sB = L * H * D if sB is None else sB
+    return lwm.Tensor4(ptr, dtype, 0, B, L, H, D, sB, sL, sH)
+
+
+def fwd(q=None, k=None, v=None, o=None, seg_q=None, seg_k=None, qo=0, ko=0, causal=1, scale=0.0):
+    L = _lib()
+    q, k, v, o = q or t4(), k or t4(), v or t4(), o or t4()
+    st = L.lwm_blockattn_fwd(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), seg_q, seg_k, qo, ko, causal, scale,
+                             ctypes.byref(o), None, None)
+    return st, L.lwm_last_error().decode()
+
+
+@pytest.mark.parametrize("kwargs,status,needle", [
+    ({"q": t4(ptr=0)}, -1, "NULL"),
+    ({"q": t4(ptr=8)}, -1, "aligned"),
+    ({"q": t4(D=64), "k": t4(D=64), "v": t4(D=64), "o": t4(D=64)}, -2, "128"),
+    ({"k": t4(H=3), "v": t4(H=3)}, -1, "mismatch"),
+    ({"v": t4(L=9)}, -1, "mismatch"),
+    ({"o": t4(L=9)}, -1, "mismatch"),
+    ({"q": t4(dtype=1)}, -2, "mixed"),
+    ({"q": t4(dtype=7)}, -2, "dtype"),
+    ({"q": t4(sL=255)}, -1, "multiples"),
+    ({"seg_q": 16}, -1, "both"),
+    ({"qo": -1}, -1, "offsets"),
+    ({"causal": 2}, -1, "causal"),
+    ({"scale": -1.0}, -1, "scale"),
+    ({"scale": float("nan")}, -1, "scale"),
+])
+def test_forward_validation(kwargs, status, needle):
+    st, msg = fwd(**kwargs)
+    assert st == status and needle in msg, (st, msg)
+
+
+def test_backward_and_ring_validation():
+    L = _lib()
+    q = t4()
+    r = ctypes.byref
+    ws = L.lwm_blockattn_bwd_workspace_size(1, 2, 8, 8, 128)
+    assert ws >= 1 * 2 * 8 * 4 and ws % 256 == 0
+    st = L.lwm_blockattn_bwd(r(q), r(q), r(q), r(q), 16, r(q), None, None, 0, 0, 1, 0.0, r(q), r(q), r(q), 256, ws - 1, None)
+    assert st == -3 and "workspace" in L.lwm_last_error().decode()
+    st = L.lwm_blockattn_bwd(r(q), r(q), r(q), r(q), None, r(q), None, None, 0, 0, 1, 0.0, r(q), r(q), r(q), 256, ws, None)
+    assert st == -1 and "lse" in L.lwm_last_error().decode()
+    f = t4(dtype=1)
+    st = L.lwm_blockattn_bwd(r(f), r(f), r(f), r(f), 16, r(f), None, None, 0, 0, 1, 0.0, r(f), r(f), r(f), 256, ws, None)
+    assert st == -2
+    oacc = t4(dtype=0)
+    st = L.lwm_ring_step(r(q), r(q), r(q), None, None, 0, 0, 1, 0.0, r(oacc), 16, None, None)
+    assert st == -1 and "float32" in L.lwm_last_error().decode()
+    oacc = t4(dtype=1, L=9)
+    st = L.lwm_ring_step(r(q), r(q), r(q), None, None, 0, 0, 1, 0.0, r(oacc), 16, None, None)
+    assert st == -1
+
+
+def test_rope_validation():
+    L = _lib()
+    r = ctypes.byref
+    x = t4()
+    for args, status in [((r(x), r(x), None, None, 0, 0.0, 0, 0, None), -1),
+                         ((r(x), r(x), None, None, 0, 1e4, 5, 0, None), -1),
+                         ((r(x), r(t4(L=4)), None, None, 0, 1e4, 0, 0, None), -1),
+                         ((r(t4(D=24)), r(t4(D=24)), None, None, 0, 1e4, 0, 0, None), -2),
+                         ((r(x), r(x), None, None, 0, 1e4, 0, 3, None), -1)]:
+        assert L.lwm_rope_apply(*args) == status, args
