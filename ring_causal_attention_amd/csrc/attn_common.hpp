@@ -1,0 +1,163 @@
+// Tile helpers shared by the attention kernels (forward, ring step, backward): LDS layouts of
+// K/V/Q/dO tiles, workgroup ordering, visibility ranges and the LDS-staged row stores.
+#pragma once
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace lwm {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * kWave;
+constexpr int D = kHeadDim;
+
+// ---------------------------------------------------------------- LDS layouts
+// Row-major tile of 128 features (16 chunks of 16 bytes per row): chunk c of row r lives at
+// r*16 + (c ^ (r & 7)), so the 8 rows read together by an MFMA operand fetch hit 8 distinct chunks.
+__device__ __forceinline__ int rm_index(int r, int c) { return r * 16 + (c ^ (r & 7)); }
+
+// Transposed tile (feature-major): row d holds the tile's rows (keys or queries) in the order
+// that makes an MFMA accumulator's rows contiguous per lane half: inside each group of 16,
+// offset o sits at position ((o>>2)&1)*8 + (o>>3)*4 + (o&3), i.e. {0..3, 8..11} then
+// {4..7, 12..15}.  A 64-row tile has 8 chunks per feature row, a 32-row tile 4; the chunk
+// index is XOR-swizzled by feature so that 8 consecutive features hit distinct banks.
+__device__ __forceinline__ int group_pos(int o) { return ((o >> 2) & 1) * 8 + (o >> 3) * 4 + (o & 3); }
+__device__ __forceinline__ int t64_index(int d, int chunk) { return d * 8 + (chunk ^ ((d & 7) ^ ((d >> 3) & 7))); }
+__device__ __forceinline__ int t32_index(int d, int chunk) { return d * 4 + (chunk ^ ((d >> 1) & 3)); }
+
+// Write 4 consecutive rows (4q .. 4q+3, q = quad index) x 8 features (8*dg .. 8*dg+7), held as
+// four 16-byte row pieces, into a transposed tile.  The quad's 4 values of one feature are 8
+// contiguous bytes (one u32x2 store per feature).
+template <int ROWS>
+__device__ __forceinline__ void write_transposed_quad(u32x4* tile, int quad, int dg, const u32x4 (&rows)[4]) {
+  const int grp = quad >> 2, qin = quad & 3;
+  const int pos = grp * 16 + (qin & 1) * 8 + (qin >> 1) * 4;  // group_pos of the quad's first row
+  const int chunk = pos >> 3, sub = (pos >> 2) & 1;
+#pragma unroll
+  for (int jd = 0; jd < 8; ++jd) {
+    const int d = dg * 8 + jd;
+    const int word = jd >> 1;
+    uint32_t w0, w1;
+    if (jd & 1) {
+      w0 = (rows[0][word] >> 16) | (rows[1][word] & 0xffff0000u);
+      w1 = (rows[2][word] >> 16) | (rows[3][word] & 0xffff0000u);
+    } else {
+      w0 = (rows[0][word] & 0xffffu) | (rows[1][word] << 16);
+      w1 = (rows[2][word] & 0xffffu) | (rows[3][word] << 16);
+    }
+    const int idx = ROWS == 64 ? t64_index(d, chunk) : t32_index(d, chunk);
+    reinterpret_cast<u32x2*>(&tile[idx])[sub] = u32x2{w0, w1};
+  }
+}
+
+// ---------------------------------------------------------------- workgroup order
+// Grid position -> (batch*head, tile).  `descending` numbers tiles from the last one (causal
+// forward: the longest query tiles first); otherwise from the first (backward over keys: the
+// earliest keys have the most queries).  When B*H is a multiple of 8, block ids congruent mod 8
+// (dispatched to the same XCD) walk one head's tiles, so they share that head's L2 working set.
+__device__ __forceinline__ void map_block(int bid, int ntiles, int BH, bool descending, int& bh, int& t) {
+  int slot_t;
+  if ((BH & 7) == 0) {
+    const int xcd = bid & 7, slot = bid >> 3;
+    bh = (slot / ntiles) * 8 + xcd;
+    slot_t = slot % ntiles;
+  } else {
+    bh = bid / ntiles;
+    slot_t = bid % ntiles;
+  }
+  t = descending ? ntiles - 1 - slot_t : slot_t;
+}
+
+// Index range [lo, hi) of the rows of `other` (length n_other, segment ids seg_other) that can
+// share a segment with rows whose ids run from s_first to s_last (ids non-decreasing).
+__device__ inline void segment_range(const int32_t* seg_other, int n_other, int32_t s_first, int32_t s_last,
+                                     int& lo, int& hi) {
+  lo = wave_lower_bound(seg_other, n_other, s_first);
+  hi = (s_last == INT32_MAX) ? n_other : wave_lower_bound(seg_other, n_other, s_last + 1);
+}
+
+// ---------------------------------------------------------------- LDS-staged row I/O
+// A wave's 32x128 accumulator (one 32-row block of an output whose rows are the lanes' columns,
+// features in the accumulator rows) is transposed through a wave-private LDS area so that global
+// stores are whole 16-byte chunks of contiguous rows.  `stage` needs 32*128*4 bytes (fp32) or
+// half of that (bf16).  Contains block-wide barriers: every wave of the block must call it.
+__device__ inline void store_rows_bf16(uint8_t* stage, const f32x16 (&acc)[4], const float mul, uint16_t* gbase,
+                                       int64_t row_stride, int rows_valid) {
+  const int lane = threadIdx.x & 63, c32 = lane & 31, h32 = lane >> 5;
+  u32x2* st2 = reinterpret_cast<u32x2*>(stage);
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int chunk = db * 4 + g;  // features db*32 + 8g .. +7; this lane half holds 4 of them
+      u32x2 w;
+      w.x = pack_bf16x2(acc[db][g * 4 + 0] * mul, acc[db][g * 4 + 1] * mul);
+      w.y = pack_bf16x2(acc[db][g * 4 + 2] * mul, acc[db][g * 4 + 3] * mul);
+      st2[(c32 * 16 + (chunk ^ (c32 & 15))) * 2 + h32] = w;
+    }
+  __syncthreads();
+  const u32x4* st4 = reinterpret_cast<const u32x4*>(stage);
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int r = it * 4 + (lane >> 4), c = lane & 15;
+    if (r < rows_valid) *reinterpret_cast<u32x4*>(gbase + r * row_stride + c * 8) = st4[r * 16 + (c ^ (r & 15))];
+  }
+  __syncthreads();
+}
+
+__device__ inline void store_rows_f32(uint8_t* stage, const f32x16 (&acc)[4], const float mul, float* gbase,
+                                      int64_t row_stride, int rows_valid) {
+  const int lane = threadIdx.x & 63, c32 = lane & 31, h32 = lane >> 5;
+  f32x4* st = reinterpret_cast<f32x4*>(stage);
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int chunk = db * 8 + g * 2 + h32;
+      f32x4 w;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[j] = acc[db][g * 4 + j] * mul;
+      st[c32 * 32 + (chunk ^ (c32 & 31))] = w;
+    }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < 16; ++it) {
+    const int r = it * 2 + (lane >> 5), c = lane & 31;
+    if (r < rows_valid) *reinterpret_cast<f32x4*>(gbase + r * row_stride + c * 4) = st[r * 32 + (c ^ (r & 31))];
+  }
+  __syncthreads();
+}
+
+__device__ inline void load_rows_f32(uint8_t* stage, f32x16 (&acc)[4], const float* gbase, int64_t row_stride,
+                                     int rows_valid) {
+  const int lane = threadIdx.x & 63, c32 = lane & 31, h32 = lane >> 5;
+  f32x4* st = reinterpret_cast<f32x4*>(stage);
+#pragma unroll
+  for (int it = 0; it < 16; ++it) {
+    const int r = it * 2 + (lane >> 5), c = lane & 31;
+    f32x4 w = {0.f, 0.f, 0.f, 0.f};
+    if (r < rows_valid) w = *reinterpret_cast<const f32x4*>(gbase + r * row_stride + c * 4);
+    st[r * 32 + (c ^ (r & 31))] = w;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int chunk = db * 8 + g * 2 + h32;
+      const f32x4 w = st[c32 * 32 + (chunk ^ (c32 & 31))];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[db][g * 4 + j] = w[j];
+    }
+  __syncthreads();
+}
+
+// Pack 8 consecutive accumulator elements (u*8 .. u*8+7) into one bf16x8 MFMA operand.
+__device__ __forceinline__ bf16x8 pack8(const f32x16& s, int u) {
+  u32x4 w;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) w[j] = pack_bf16x2(s[u * 8 + 2 * j], s[u * 8 + 2 * j + 1]);
+  return as_bf16x8(w);
+}
+
+}  // namespace lwm

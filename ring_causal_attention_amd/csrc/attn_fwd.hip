@@ -26,43 +26,21 @@
 //    pairs are dealt to the 8 XCDs so the query tiles sharing one head's K/V run on one L2.
 #include <float.h>
 
-#include "common.hpp"
-#include "kernels.hpp"
+#include "attn_common.hpp"
 
 namespace lwm {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * kWave;
-constexpr int BN = 64;  // keys per tile (bf16 path)
-constexpr int D = kHeadDim;
+constexpr int BN = 64;                 // keys per tile (bf16 path)
 constexpr float kRescaleSlack = 8.0f;  // log2 units: p <= 2^8 between rescales
 
 struct SmemBf16 {
-  u32x4 k[2][BN * 16];        // [stage][key][16 chunks], chunk c of key r at r*16 + (c ^ (r & 7))
-  u32x4 vt[2][D * (BN / 8)];  // [stage][feature][8 chunks], swizzled by vt_swz(d)
+  u32x4 k[2][BN * 16];        // [stage] row-major K tile, rm_index(key, chunk)
+  u32x4 vt[2][D * (BN / 8)];  // [stage] transposed V tile, t64_index(feature, chunk)
   int32_t seg[2][BN];
 };
 static_assert(sizeof(SmemBf16) <= 80 * 1024, "two workgroups per CU must fit in LDS");
-
-__device__ __forceinline__ int vt_swz(int d) { return (d & 7) ^ ((d >> 3) & 7); }
-
-// Position of key offset o (0..15) inside its 16-key group in the transposed V tile: the
-// accumulator rows a lane half owns ({0..3, 8..11} or {4..7, 12..15}) become contiguous.
-__device__ __forceinline__ int group_pos(int o) { return ((o >> 2) & 1) * 8 + (o >> 3) * 4 + (o & 3); }
-
-// Grid position -> (batch*head, query tile).  Longest causal tiles first; with (B*H) % 8 == 0
-// consecutive dispatch slots of one XCD (block ids congruent mod 8) walk one head's tiles.
-__device__ __forceinline__ void map_block(int bid, int nqt, int BH, int& bh, int& qt) {
-  if ((BH & 7) == 0) {
-    const int xcd = bid & 7, slot = bid >> 3;
-    bh = (slot / nqt) * 8 + xcd;
-    qt = nqt - 1 - (slot % nqt);
-  } else {
-    bh = bid / nqt;
-    qt = nqt - 1 - (bid % nqt);
-  }
-}
+static_assert(sizeof(SmemBf16) >= kWaves * 32 * D * 4, "epilogue staging must fit");
 
 // Key range [kbeg, kend) that can be visible to query rows [r0, r1] (inclusive).
 __device__ inline void key_range(const FwdParams& p, int b, int r0, int r1, int& kbeg, int& kend) {
@@ -73,90 +51,12 @@ __device__ inline void key_range(const FwdParams& p, int b, int r0, int r1, int&
     kend = (int)max<int64_t>(0, min<int64_t>(kend, lim));
   }
   if (p.seg_q) {
-    const int32_t* sk = p.seg_k + (int64_t)b * p.Lk;
-    const int32_t s0 = p.seg_q[(int64_t)b * p.Lq + r0];
-    const int32_t s1 = p.seg_q[(int64_t)b * p.Lq + r1];
-    kbeg = max(kbeg, wave_lower_bound(sk, p.Lk, s0));
-    kend = min(kend, s1 == INT32_MAX ? p.Lk : wave_lower_bound(sk, p.Lk, s1 + 1));
+    int lo, hi;
+    segment_range(p.seg_k + (int64_t)b * p.Lk, p.Lk, p.seg_q[(int64_t)b * p.Lq + r0], p.seg_q[(int64_t)b * p.Lq + r1],
+                  lo, hi);
+    kbeg = max(kbeg, lo);
+    kend = min(kend, hi);
   }
-}
-
-// ---------------------------------------------------------------------------- epilogue staging
-// Rows of a wave's O^T accumulator (lane = query column) are transposed through LDS so that
-// global stores are whole 16-byte chunks of contiguous rows.
-template <int QB>
-__device__ inline void store_rows_bf16(uint8_t* stage, const f32x16 (&acc)[4], const float inv,
-                                       uint16_t* gbase, int64_t row_stride, int rows_valid) {
-  // stage: 32 rows x 16 chunks (16 B) per wave, chunk c of row r at r*16 + (c ^ (r & 15))
-  const int lane = threadIdx.x & 63, c32 = lane & 31, h32 = lane >> 5;
-  u32x2* st2 = reinterpret_cast<u32x2*>(stage);
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int chunk = db * 4 + g;  // features db*32 + g*8 .. +7; this half holds 4 of them
-      u32x2 w;
-      w.x = pack_bf16x2(acc[db][g * 4 + 0] * inv, acc[db][g * 4 + 1] * inv);
-      w.y = pack_bf16x2(acc[db][g * 4 + 2] * inv, acc[db][g * 4 + 3] * inv);
-      st2[(c32 * 16 + (chunk ^ (c32 & 15))) * 2 + h32] = w;
-    }
-  __syncthreads();
-  const u32x4* st4 = reinterpret_cast<const u32x4*>(stage);
-#pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const int r = it * 4 + (lane >> 4), c = lane & 15;
-    if (r < rows_valid)
-      *reinterpret_cast<u32x4*>(gbase + r * row_stride + c * 8) = st4[r * 16 + (c ^ (r & 15))];
-  }
-  __syncthreads();
-}
-
-__device__ inline void store_rows_f32(uint8_t* stage, const f32x16 (&acc)[4], const float inv,
-                                      float* gbase, int64_t row_stride, int rows_valid) {
-  // stage: 32 rows x 32 chunks (16 B), chunk c of row r at r*32 + (c ^ (r & 31))
-  const int lane = threadIdx.x & 63, c32 = lane & 31, h32 = lane >> 5;
-  f32x4* st = reinterpret_cast<f32x4*>(stage);
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int chunk = db * 8 + g * 2 + h32;
-      f32x4 w;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) w[j] = acc[db][g * 4 + j] * inv;
-      st[c32 * 32 + (chunk ^ (c32 & 31))] = w;
-    }
-  __syncthreads();
-#pragma unroll
-  for (int it = 0; it < 16; ++it) {
-    const int r = it * 2 + (lane >> 5), c = lane & 31;
-    if (r < rows_valid) *reinterpret_cast<f32x4*>(gbase + r * row_stride + c * 4) = st[r * 32 + (c ^ (r & 31))];
-  }
-  __syncthreads();
-}
-
-__device__ inline void load_rows_f32(uint8_t* stage, f32x16 (&acc)[4], const float* gbase,
-                                     int64_t row_stride, int rows_valid) {
-  const int lane = threadIdx.x & 63, c32 = lane & 31, h32 = lane >> 5;
-  f32x4* st = reinterpret_cast<f32x4*>(stage);
-#pragma unroll
-  for (int it = 0; it < 16; ++it) {
-    const int r = it * 2 + (lane >> 5), c = lane & 31;
-    f32x4 w = {0.f, 0.f, 0.f, 0.f};
-    if (r < rows_valid) w = *reinterpret_cast<const f32x4*>(gbase + r * row_stride + c * 4);
-    st[r * 32 + (c ^ (r & 31))] = w;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int chunk = db * 8 + g * 2 + h32;
-      const f32x4 w = st[c32 * 32 + (chunk ^ (c32 & 31))];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[db][g * 4 + j] = w[j];
-    }
-  __syncthreads();
 }
 
 // ---------------------------------------------------------------------------- bf16 kernel
@@ -170,7 +70,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdParams p)
   const int c32 = lane & 31, h32 = lane >> 5;
   const int nqt = (p.Lq + BM - 1) / BM;
   int bh, qt;
-  map_block(blockIdx.x, nqt, p.B * p.H, bh, qt);
+  map_block(blockIdx.x, nqt, p.B * p.H, true, bh, qt);
   const int b = bh / p.H, hh = bh - b * p.H;
   const int q0 = qt * BM;
   const int qlast = min(q0 + BM, p.Lq) - 1;
@@ -264,27 +164,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdParams p)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int key = r * 16 + ld_key;
-      sm.k[st][key * 16 + (ld_c ^ (key & 7))] = kst[r];
+      sm.k[st][rm_index(key, ld_c)] = kst[r];
     }
-    // V: transpose 4 keys x 8 features into 8 features x 4 keys (8 bytes each)
-    const int quad = ld_kq & 3, grp = ld_kq >> 2;
-    const int chunk = grp * 2 + (quad & 1);
-    const int sub = quad >> 1;
-#pragma unroll
-    for (int jd = 0; jd < 8; ++jd) {
-      const int d = ld_dg * 8 + jd;
-      const int word = jd >> 1;
-      uint32_t w0, w1;
-      if (jd & 1) {
-        w0 = (vst[0][word] >> 16) | (vst[1][word] & 0xffff0000u);
-        w1 = (vst[2][word] >> 16) | (vst[3][word] & 0xffff0000u);
-      } else {
-        w0 = (vst[0][word] & 0xffffu) | (vst[1][word] << 16);
-        w1 = (vst[2][word] & 0xffffu) | (vst[3][word] << 16);
-      }
-      u32x2* dst = reinterpret_cast<u32x2*>(&sm.vt[st][d * 8 + (chunk ^ vt_swz(d))]);
-      dst[sub] = u32x2{w0, w1};
-    }
+    // V: 4 keys x 8 features -> feature-major
+    write_transposed_quad<BN>(sm.vt[st], ld_kq, ld_dg, vst);
     if (segs && tid < BN) sm.seg[st][tid] = segst;
   };
 
@@ -327,7 +210,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdParams p)
         for (int kb = 0; kb < 2; ++kb) {
           const int key = kb * 32 + c32;
           const int chunk = 2 * sd + h32;
-          const bf16x8 a = as_bf16x8(sm.k[st][key * 16 + (chunk ^ (key & 7))]);
+          const bf16x8 a = as_bf16x8(sm.k[st][rm_index(key, chunk)]);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma_32x32x16(a, qreg[qb][sd], s[kb][qb]);
         }
@@ -395,9 +278,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdParams p)
             for (int j = 0; j < 4; ++j) {
               const float e0 = fast_exp2(__builtin_fmaf(s[kb][qb][u * 8 + 2 * j], p.scale_log2, -moff));
               const float e1 = fast_exp2(__builtin_fmaf(s[kb][qb][u * 8 + 2 * j + 1], p.scale_log2, -moff));
-              packed[j] = pack_bf16x2(e0, e1);
-              lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed[j]),
-                                                     bf16x2{(__bf16)1.0f, (__bf16)1.0f}, lsum, false);
+              const uint32_t word = pack_bf16x2(e0, e1);
+              lsum = sum_bf16x2(word, lsum);
+              packed[j] = word;
             }
             pb[kb][u][qb] = as_bf16x8(packed);
           }
@@ -414,7 +297,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdParams p)
           for (int db = 0; db < 4; ++db) {
             const int d = db * 32 + c32;
             const int chunk = g * 2 + h32;
-            const bf16x8 a = as_bf16x8(sm.vt[st][d * 8 + (chunk ^ vt_swz(d))]);
+            const bf16x8 a = as_bf16x8(sm.vt[st][t64_index(d, chunk)]);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma_32x32x16(a, pb[kb][u][qb], acc[qb][db]);
           }
@@ -437,7 +320,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdParams p)
     const float inv = any ? 1.f / lt : 0.f;
     const float lse = any ? (m[qb] + log2f(lt)) * kLn2 : -INFINITY;
     if (!ring) {
-      if (og) store_rows_bf16<QB>(stage_w, acc[qb], inv, og + b * p.so.b + hh * p.so.h + r0 * p.so.l, p.so.l, rows_valid);
+      if (og) store_rows_bf16(stage_w, acc[qb], inv, og + b * p.so.b + hh * p.so.h + r0 * p.so.l, p.so.l, rows_valid);
       if (lse_row && h32 == 0 && qrow[qb] < p.Lq) lse_row[qrow[qb]] = lse;
     } else {
       float* lag = p.lse_acc + ((int64_t)b * p.H + hh) * p.Lq;
@@ -449,12 +332,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdParams p)
         const float sc = untouched ? 1.f : inv;
         store_rows_f32(stage_w, acc[qb], sc, oag, p.soa.l, rows_valid);
         if (h32 == 0 && qrow[qb] < p.Lq && !untouched) lag[qrow[qb]] = lse;
-        if (ofg) store_rows_bf16<QB>(stage_w, acc[qb], sc, ofg, p.so.l, rows_valid);
+        if (ofg) store_rows_bf16(stage_w, acc[qb], sc, ofg, p.so.l, rows_valid);
       } else if (ofg) {
         // nothing visible in this shard for the whole tile: the bf16 copy is the state itself
         f32x16 tmp[4];
         load_rows_f32(stage_w, tmp, oag, p.soa.l, rows_valid);
-        store_rows_bf16<QB>(stage_w, tmp, 1.f, ofg, p.so.l, rows_valid);
+        store_rows_bf16(stage_w, tmp, 1.f, ofg, p.so.l, rows_valid);
       }
     }
   }
@@ -479,7 +362,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_f32_kernel(FwdParams p) 
   const int c32 = lane & 31, h32 = lane >> 5;
   const int nqt = (p.Lq + BM - 1) / BM;
   int bh, qt;
-  map_block(blockIdx.x, nqt, p.B * p.H, bh, qt);
+  map_block(blockIdx.x, nqt, p.B * p.H, true, bh, qt);
   const int b = bh / p.H, hh = bh - b * p.H;
   const int q0 = qt * BM;
   const int qlast = min(q0 + BM, p.Lq) - 1;

@@ -30,6 +30,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, p);
 }
 
+// acc + lo + hi of a packed bf16 pair (v_dot2_f32_bf16 against (1, 1)).  Takes the pair as a
+// scalar word: feeding it an element of a vector through bit_cast has been lowered to the wrong
+// register by this compiler.
+__device__ __forceinline__ float sum_bf16x2(uint32_t pair, float acc) {
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  bf16x2 v;
+  __builtin_memcpy(&v, &pair, sizeof(v));
+  return __builtin_amdgcn_fdot2_f32_bf16(v, ones, acc, false);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ u32x4 as_u32x4(bf16x8 v) { return __builtin_bit_cast(u32x4, v); }
 

@@ -33,12 +33,22 @@ def normal(seed: int, tensor: str, shape, shard: int | None = None) -> np.ndarra
 
 
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round float32 to bfloat16 (round-to-nearest-even); returns the uint16 bit patterns."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    # NaN never occurs in N(0,1) draws; keep the rounding rule plain.
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return rounded.astype(np.uint16)
+    """Round float32 to bfloat16 (round-to-nearest-even); returns the uint16 bit patterns.
+
+    Works on the 32-bit patterns: adding 0x7FFF plus the lowest kept bit and truncating is
+    round-to-nearest-even for every finite value (no finite pattern overflows 32 bits).
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    out = np.empty(u.shape, dtype=np.uint16)
+    flat_u, flat_o = u.reshape(-1), out.reshape(-1)
+    step = 1 << 24
+    for i in range(0, flat_u.size, step):
+        c = flat_u[i:i + step]
+        r = (c >> 16) & 1
+        r += c
+        r += 0x7FFF
+        flat_o[i:i + step] = r >> 16
+    return out
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
@@ -83,3 +93,10 @@ def random_segment_ids(seed: int, batch: int, length: int, max_len: int) -> np.n
             t += n
             sid += 1
     return out
+
+
+def normal_many(requests, threads: int = 8) -> list[np.ndarray]:
+    """Several ``normal`` draws in parallel threads; ``requests`` holds (seed, tensor, shape, shard)."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
+        return list(ex.map(lambda r: normal(*r), requests))

@@ -1,0 +1,107 @@
+"""lwm_blockattn_bwd (and the full training-step composition) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from ring_causal_attention_amd import lwm, path, synth
+from tests.gpu_utils import GRAD_REL_FRO, dev, exact_host, host, need_gpu, note, rel_fro, seg_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def bwd_case(B, Lq, Lk, H, seed, seg=None, q_offset=0, k_offset=0, causal=True):
+    note(f"bwd B={B} Lq={Lq} Lk={Lk} H={H} seg={seg is not None} q_off={q_offset} k_off={k_offset} causal={causal}")
+    q, k, v = (synth.normal(seed, t, (B, L, H, 128)) for t, L in (("q", Lq), ("k", Lk), ("v", Lk)))
+    do = synth.normal(seed, "do", (B, Lq, H, 128))
+    sq = sk = None
+    if seg is not None:
+        sq, sk = seg
+    qd, kd, vd, dod = dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), dev(do, "bf16")
+    sqd = None if sq is None else seg_dev(sq)
+    skd = None if sk is None else seg_dev(sk)
+    o, lse = lwm.lwm_blockattn_fwd(qd, kd, vd, sqd, skd, q_offset, k_offset, causal)
+    dq, dk, dv = lwm.lwm_blockattn_bwd(qd, kd, vd, o, lse, dod, sqd, skd, q_offset, k_offset, causal)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv = oracle.attention_bwd(exact_host(q, "bf16"), exact_host(k, "bf16"), exact_host(v, "bf16"),
+                                         exact_host(do, "bf16"), sq, sk, q_offset, k_offset, causal)
+    out = {}
+    for name, g, r in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+        gg = host(g)
+        assert np.all(np.isfinite(gg)), name
+        if np.linalg.norm(r) == 0:
+            assert np.all(gg == 0), name
+            continue
+        e = rel_fro(gg, r)
+        out[name] = e
+        assert e <= GRAD_REL_FRO, (name, e)
+    return out
+
+
+@pytest.mark.parametrize("L", [1, 2, 63, 64, 65, 127, 129, 300, 1000])
+def test_causal_lengths(L):
+    need_gpu()
+    bwd_case(1, L, L, 2, 2000 + L)
+
+
+@pytest.mark.parametrize("L", [200, 777])
+def test_packed_segments(L):
+    need_gpu()
+    seg = synth.random_segment_ids(L + 1, 2, L, 150)
+    bwd_case(2, L, L, 2, 2100 + L, seg=(seg, seg))
+
+
+@pytest.mark.parametrize("offsets,lens", [((200, 0), (150, 350)), ((0, 50), (200, 200)), ((333, 17), (129, 400)),
+                                          ((64, 64), (100, 100))])
+def test_offsets(offsets, lens):
+    need_gpu()
+    bwd_case(1, lens[0], lens[1], 2, 2200 + sum(offsets), q_offset=offsets[0], k_offset=offsets[1])
+
+
+def test_noncausal_and_heads():
+    need_gpu()
+    bwd_case(1, 190, 77, 2, 2301, causal=False)
+    bwd_case(2, 160, 160, 4, 2302)  # B*H multiple of 8
+
+
+def test_bwd_deterministic():
+    need_gpu()
+    note("bwd bitwise determinism")
+    q, k, v, do = (dev(synth.normal(2400, t, (1, 500, 4, 128)), "bf16") for t in ("q", "k", "v", "do"))
+    o, lse = lwm.lwm_blockattn_fwd(q, k, v)
+    ref = lwm.lwm_blockattn_bwd(q, k, v, o, lse, do)
+    for _ in range(3):
+        got = lwm.lwm_blockattn_bwd(q, k, v, o, lse, do)
+        assert all(torch.equal(a, b) for a, b in zip(got, ref))
+
+
+def test_training_step_composition():
+    need_gpu()
+    note("training step: rope -> fwd -> bwd -> inverse rope, with packing")
+    B, L, H, theta = 1, 400, 2, 1.0e6
+    seg = synth.segment_ids_from_lengths([150, 1, 249])
+    q, k, v, do = (synth.normal(2500, t, (B, L, H, 128)) for t in ("q", "k", "v", "do"))
+    o, lse, dq, dk, dv = path.training_step(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), dev(do, "bf16"), theta,
+                                            seg=seg_dev(seg))
+    torch.cuda.synchronize()
+    pos = oracle.positions(B, L, 0, seg)
+    ro, rl, rdq, rdk, rdv = oracle.training_step(*(exact_host(x, "bf16") for x in (q, k, v, do)), pos, pos, theta,
+                                                 "half", seg, seg)
+    assert np.max(np.abs(host(o) - ro)) <= 2e-2
+    for g, r in ((dq, rdq), (dk, rdk), (dv, rdv)):
+        assert rel_fro(host(g), r) <= GRAD_REL_FRO
+
+
+def test_gradient_identities_hold_on_gpu():
+    need_gpu()
+    note("sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i on the GPU output")
+    B, L, H = 1, 2048, 4
+    q, k, v, do = (synth.normal(2600, t, (B, L, H, 128)) for t in ("q", "k", "v", "do"))
+    qd, kd, vd, dod = (dev(x, "bf16") for x in (q, k, v, do))
+    o, lse = lwm.lwm_blockattn_fwd(qd, kd, vd)
+    dq, dk, dv = lwm.lwm_blockattn_bwd(qd, kd, vd, o, lse, dod)
+    torch.cuda.synchronize()
+    sdk = host(dk).sum(axis=1)
+    assert np.linalg.norm(sdk) <= 2e-2 * np.linalg.norm(host(dk))
+    sdv, sdo = host(dv).sum(axis=1), exact_host(do, "bf16").sum(axis=1)
+    assert np.linalg.norm(sdv - sdo) <= 1e-2 * np.linalg.norm(sdo)

@@ -48,7 +48,7 @@ def test_ring_order_invariance():
     a, _, la = path.ring_forward(qd, kd, vd, order, 96, q_off)
     b, _, lb = path.ring_forward(qd, kd, vd, order[::-1], 96, q_off)
     torch.cuda.synchronize()
-    assert np.max(np.abs(host(a) - host(b))) <= 2e-2 and np.max(np.abs(host(la) - host(lb))) <= 1e-4
+    assert np.max(np.abs(host(a) - host(b))) <= 2e-2 and np.max(np.abs(host(la) - host(lb))) <= LSE_BF16
 
 
 def test_unvisited_rows_keep_state_bitwise():

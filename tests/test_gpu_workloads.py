@@ -1,0 +1,162 @@
+"""The five workloads at full size, run exactly as bench.py runs them, against the oracle.
+
+Full-size outputs are checked on sampled rows the oracle computes one by one (every row of the
+small fp32 workload; one full head for the training step's gradients), plus properties that hold
+at any size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from ring_causal_attention_amd import configs, lwm, path, workloads
+from ring_causal_attention_amd.synth import round_to_bf16
+from tests.gpu_utils import (BF16_MAX_ABS, BF16_MEAN_ABS, FP32_MAX_ABS, GRAD_REL_FRO, LSE_BF16, errors, host,
+                             need_gpu, note, rel_fro)
+
+pytestmark = pytest.mark.gpu
+W = configs.WORKLOADS
+
+
+def exact(x, dtype):
+    return (round_to_bf16(x) if dtype == "bf16" else x).astype(np.float64)
+
+
+def sample_rows(L, extra=(), n_random=24, seed=0):
+    base = {0, 1, 2, 63, 64, 127, 128, 129, L // 2, L - 2, L - 1}
+    base |= {int(r) for r in extra if 0 <= r < L}
+    base |= set(np.random.default_rng(seed).integers(0, L, n_random).tolist())
+    return sorted(base)
+
+
+def oracle_rows(q, k, v, rows, theta, dtype, pos_q, pos_k, seg=None, q_offset=0, k_offset=0, heads=None):
+    """Oracle O, lse for the chosen query rows (RoPE and attention in float64), one row at a time."""
+    hs = slice(None) if heads is None else list(heads)
+    maxlim = min(k.shape[1], q_offset + max(rows) - k_offset + 1)
+    kr_all = oracle.rope(exact(k[:, :maxlim][:, :, hs], dtype), pos_k[:, :maxlim], theta)
+    vr_all = exact(v[:, :maxlim][:, :, hs], dtype)
+    o_rows, l_rows = [], []
+    for r in rows:
+        lim = min(k.shape[1], q_offset + r - k_offset + 1)
+        qr = oracle.rope(exact(q[:, r:r + 1][:, :, hs], dtype), pos_q[:, r:r + 1], theta)
+        sq = None if seg is None else seg[:, r:r + 1]
+        sk = None if seg is None else seg[:, :lim]
+        o, l = oracle.attention_fwd(qr, kr_all[:, :lim], vr_all[:, :lim], sq, sk, q_offset + r, k_offset, True)
+        o_rows.append(o[:, 0])
+        l_rows.append(l[:, :, 0])
+    return np.stack(o_rows, 1), np.stack(l_rows, 2)
+
+
+def check_rows(o_dev, lse_dev, ref_o, ref_l, rows, dtype, heads=None):
+    hs = slice(None) if heads is None else list(heads)
+    got = host(o_dev[:, rows][:, :, hs])
+    gl = host(lse_dev[:, hs][:, :, rows]) if lse_dev is not None else None
+    mx, mean = errors(got, ref_o)
+    if dtype == "bf16":
+        assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (mx, mean)
+    else:
+        assert mx <= FP32_MAX_ABS, mx
+    if gl is not None:
+        assert np.max(np.abs(gl - ref_l)) <= (LSE_BF16 if dtype == "bf16" else 1e-5)
+    return mx, mean
+
+
+def test_causal_fp32_L1024_full():
+    need_gpu()
+    w = W["causal_fp32_L1024"]
+    note(f"workload {w.name}")
+    h = workloads.host_inputs(w)
+    d = workloads.device_inputs(h)
+    o, lse, _, _ = path.attention_forward(d["q"], d["k"], d["v"], w.theta)
+    torch.cuda.synchronize()
+    pos = oracle.positions(w.B, w.Lq)
+    qr, kr = oracle.rope(exact(h["q"], "fp32"), pos, w.theta), oracle.rope(exact(h["k"], "fp32"), pos, w.theta)
+    ro, rl = oracle.attention_fwd(qr, kr, exact(h["v"], "fp32"))
+    mx, _ = errors(host(o), ro)
+    assert mx <= FP32_MAX_ABS, mx
+    assert np.max(np.abs(host(lse) - rl)) <= 1e-5
+
+
+def test_llama7b_fwd_L32768_sampled():
+    need_gpu()
+    w = W["llama7b_fwd_L32768"]
+    note(f"workload {w.name}")
+    h = workloads.host_inputs(w)
+    d = workloads.device_inputs(h)
+    o, lse, _, _ = path.attention_forward(d["q"], d["k"], d["v"], w.theta)
+    torch.cuda.synchronize()
+    assert not bool(torch.isnan(o).any())
+    rows = sample_rows(w.Lq, seed=2)
+    pos = oracle.positions(w.B, w.Lq)
+    ro, rl = oracle_rows(h["q"], h["k"], h["v"], rows, w.theta, "bf16", pos, pos)
+    check_rows(o, lse, ro, rl, rows, "bf16")
+    # row 0 sees only key 0: O_0 = V_0 exactly
+    assert torch.equal(o[:, 0].float(), d["v"][:, 0].float())
+
+
+def test_packed_L65536_sampled():
+    need_gpu()
+    w = W["packed_L65536"]
+    note(f"workload {w.name}")
+    h = workloads.host_inputs(w)
+    d = workloads.device_inputs(h)
+    o, lse, _, _ = path.attention_forward(d["q"], d["k"], d["v"], w.theta, seg=d["seg"])
+    torch.cuda.synchronize()
+    lens = w.segment_lengths()
+    starts = np.cumsum([0] + lens[:-1])
+    ends = starts + np.array(lens) - 1
+    rows = sample_rows(w.Lq, extra=list(starts) + list(ends), seed=3)
+    pos = oracle.positions(w.B, w.Lq, 0, h["seg"])
+    ro, rl = oracle_rows(h["q"], h["k"], h["v"], rows, w.theta, "bf16", pos, pos, seg=h["seg"])
+    check_rows(o, lse, ro, rl, rows, "bf16")
+    # every segment start returns its own V row bit for bit
+    assert torch.equal(o[:, starts].float(), d["v"][:, starts].float())
+
+
+def test_ring_share_1M_sampled():
+    need_gpu()
+    w = W["ring_share_1M"]
+    note(f"workload {w.name}")
+    h = workloads.host_inputs(w)
+    d = workloads.device_inputs(h)
+    S, r = w.Lq, w.ring_index
+    qr = lwm.lwm_rope_apply(d["q"], pos_offset=w.q_offset, theta=w.theta)
+    kr = {j: lwm.lwm_rope_apply(x, pos_offset=j * S, theta=w.theta) for j, x in d["k_shards"].items()}
+    o, o_acc, lse = path.ring_forward(qr, kr, d["v_shards"], w.ring_order(), S, w.q_offset)
+    torch.cuda.synchronize()
+    heads = [0, 5]
+    rows = sample_rows(S, n_random=12, seed=4)
+    k_all = np.concatenate([h["k_shards"][j] for j in range(r + 1)], axis=1)
+    v_all = np.concatenate([h["v_shards"][j] for j in range(r + 1)], axis=1)
+    pos_q = oracle.positions(w.B, S, w.q_offset)
+    pos_k = oracle.positions(w.B, k_all.shape[1])
+    ro, rl = oracle_rows(h["q"], k_all, v_all, rows, w.theta, "bf16", pos_q, pos_k, q_offset=w.q_offset,
+                         heads=heads)
+    check_rows(o, lse, ro, rl, rows, "bf16", heads=heads)
+
+
+def test_train_step_L32768_one_head():
+    need_gpu()
+    w = W["train_step_L32768"]
+    note(f"workload {w.name}")
+    h = workloads.host_inputs(w)
+    d = workloads.device_inputs(h)
+    o, lse, dq, dk, dv = path.training_step(d["q"], d["k"], d["v"], d["do"], w.theta)
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv):
+        assert not bool(torch.isnan(t).any())
+    # exact identities of the gradient at full size, all heads: sum_j dV_j = sum_i dO_i
+    sdv = dv.float().sum(dim=1).cpu().numpy()
+    sdo = exact(h["do"], "bf16").sum(axis=1)
+    assert np.linalg.norm(sdv - sdo) <= 1e-2 * np.linalg.norm(sdo)
+    # one full head against the oracle's training step (forward, backward, inverse RoPE)
+    hh = 7
+    pos = oracle.positions(w.B, w.Lq)
+    sl = lambda x: exact(x[:, :, hh:hh + 1], "bf16")
+    ro, rl, rdq, rdk, rdv = oracle.training_step(sl(h["q"]), sl(h["k"]), sl(h["v"]), sl(h["do"]), pos, pos,
+                                                 w.theta, "half")
+    mx, mean = errors(host(o[:, :, hh:hh + 1]), ro)
+    assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (mx, mean)
+    for name, g, ref in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+        e = rel_fro(host(g[:, :, hh:hh + 1]), ref)
+        assert e <= GRAD_REL_FRO, (name, e)
