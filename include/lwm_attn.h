@@ -156,6 +156,20 @@ int lwm_ring_step(const lwm_tensor4* q, const lwm_tensor4* k_shard, const lwm_te
                   int32_t causal, float scale, const lwm_tensor4* o_acc, float* lse_acc,
                   const lwm_tensor4* o_final, void* stream);
 
+/*
+ * Kernel timing (instrumentation, not part of the method).  While enabled, every kernel the
+ * library launches is bracketed by two HIP events recorded on its launch stream, so durations
+ * are those of the kernels themselves.  lwm_profile_count / lwm_profile_get wait for the
+ * recorded events, then report per kernel name the summed milliseconds and launch count since
+ * the last lwm_profile_reset.  Names returned stay valid until the next reset.  Host-side state
+ * only (HIP events, no device memory); thread-safe.  Returns LWM_OK, LWM_ERR_INVALID_ARG for a
+ * bad index or NULL output, LWM_ERR_HIP if an event could not be resolved.
+ */
+int lwm_profile_enable(int32_t on);
+int lwm_profile_reset(void);
+int lwm_profile_count(void);
+int lwm_profile_get(int32_t index, const char** name, double* total_ms, int64_t* launches);
+
 #ifdef __cplusplus
 }
 #endif

@@ -18,7 +18,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblwm_attn.so")
 ARCH = "gfx950"
 
-SOURCES = ["abi.cpp", "rope.hip", "attn_fwd.hip", "attn_bwd.hip"]
+SOURCES = ["abi.cpp", "profile.cpp", "rope.hip", "attn_fwd.hip", "attn_bwd.hip"]
 
 # Packed-FP32 VALU forms are disabled for device code; the host pass ignores the feature.
 HIPCC_FLAGS = [
@@ -64,3 +64,16 @@ def build(verbose: bool = True, save_temps: bool = False) -> str:
 
 if __name__ == "__main__":
     build(save_temps="--save-temps" in sys.argv)
+
+
+def sources_digest() -> str:
+    """sha256 over the kernel sources and headers (identifies the code a measurement was taken on)."""
+    import hashlib
+    hsh = hashlib.sha256()
+    names = sorted(n for n in os.listdir(CSRC) if n.endswith((".hip", ".hpp", ".cpp")))
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            hsh.update(n.encode() + b"\0" + f.read())
+    with open(os.path.join(ROOT, "include", "lwm_attn.h"), "rb") as f:
+        hsh.update(f.read())
+    return hsh.hexdigest()

@@ -18,6 +18,7 @@
 //  Recomputing S and dP in both kernels costs two extra products over the five the method needs;
 //  in exchange no partial dQ is ever written to or reduced through memory.
 #include "attn_common.hpp"
+#include "profile.hpp"
 
 namespace lwm {
 namespace {
@@ -403,13 +404,13 @@ hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t stream) {
   if (p.B == 0 || p.H == 0) return hipSuccess;
   if (p.Lq > 0) {
     const int64_t rows = (int64_t)p.B * p.Lq * p.H;
-    hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, p);
+    LWM_LAUNCH("bwd_delta", bwd_delta_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), stream, p);
     const int nqt = (p.Lq + 127) / 128;
-    hipLaunchKernelGGL(bwd_dq_kernel, dim3(nqt * p.B * p.H), dim3(kThreads), 0, stream, p);
+    LWM_LAUNCH("bwd_dq", bwd_dq_kernel, dim3(nqt * p.B * p.H), dim3(kThreads), stream, p);
   }
   if (p.Lk > 0) {
     const int nkt = (p.Lk + 127) / 128;
-    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(nkt * p.B * p.H), dim3(kThreads), 0, stream, p);
+    LWM_LAUNCH("bwd_dkdv", bwd_dkdv_kernel, dim3(nkt * p.B * p.H), dim3(kThreads), stream, p);
   }
   return hipGetLastError();
 }

@@ -27,6 +27,7 @@
 #include <float.h>
 
 #include "attn_common.hpp"
+#include "profile.hpp"
 
 namespace lwm {
 namespace {
@@ -497,10 +498,11 @@ hipError_t launch_attn_fwd(const FwdParams& p, bool bf16, hipStream_t stream) {
   if (bf16) {
     constexpr int QB = 1, BM = kWaves * 32 * QB;
     const int nqt = (p.Lq + BM - 1) / BM;
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<QB>, dim3(nqt * p.B * p.H), dim3(kThreads), 0, stream, p);
+    LWM_LAUNCH(p.mode == 1 ? "ring_step_bf16" : "attn_fwd_bf16", attn_fwd_bf16_kernel<QB>, dim3(nqt * p.B * p.H),
+               dim3(kThreads), stream, p);
   } else {
     const int nqt = (p.Lq + 127) / 128;
-    hipLaunchKernelGGL(attn_fwd_f32_kernel, dim3(nqt * p.B * p.H), dim3(kThreads), 0, stream, p);
+    LWM_LAUNCH("attn_fwd_f32", attn_fwd_f32_kernel, dim3(nqt * p.B * p.H), dim3(kThreads), stream, p);
   }
   return hipGetLastError();
 }

@@ -9,6 +9,7 @@
 // by every head instead of being repeated per element.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "profile.hpp"
 
 namespace lwm {
 namespace {
@@ -152,8 +153,8 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(RopeParams p) {
 hipError_t launch_rope(const RopeParams& p, bool bf16, hipStream_t stream) {
   if (p.L == 0 || p.B == 0 || p.H == 0) return hipSuccess;
   dim3 grid((p.L + kTok - 1) / kTok, p.B);
-  if (bf16) hipLaunchKernelGGL(rope_kernel<uint16_t>, grid, dim3(kThreads), 0, stream, p);
-  else hipLaunchKernelGGL(rope_kernel<float>, grid, dim3(kThreads), 0, stream, p);
+  if (bf16) LWM_LAUNCH("rope_bf16", rope_kernel<uint16_t>, grid, dim3(kThreads), stream, p);
+  else LWM_LAUNCH("rope_f32", rope_kernel<float>, grid, dim3(kThreads), stream, p);
   return hipGetLastError();
 }
 

@@ -35,7 +35,8 @@ class Tensor4(ctypes.Structure):
 
 _lib = None
 EXPORTS = ["lwm_abi_version", "lwm_last_error", "lwm_rope_apply", "lwm_blockattn_fwd",
-           "lwm_blockattn_bwd_workspace_size", "lwm_blockattn_bwd", "lwm_ring_step"]
+           "lwm_blockattn_bwd_workspace_size", "lwm_blockattn_bwd", "lwm_ring_step",
+           "lwm_profile_enable", "lwm_profile_reset", "lwm_profile_count", "lwm_profile_get"]
 
 
 def lib() -> ctypes.CDLL:
@@ -62,6 +63,14 @@ def lib() -> ctypes.CDLL:
     L.lwm_blockattn_bwd.argtypes = [P, P, P, P, VP, P, VP, VP, I64, I64, I32, F32, P, P, P, VP, ctypes.c_size_t, VP]
     L.lwm_ring_step.restype = ctypes.c_int
     L.lwm_ring_step.argtypes = [P, P, P, VP, VP, I64, I64, I32, F32, P, VP, P, VP]
+    L.lwm_profile_enable.restype = ctypes.c_int
+    L.lwm_profile_enable.argtypes = [I32]
+    L.lwm_profile_reset.restype = ctypes.c_int
+    L.lwm_profile_reset.argtypes = []
+    L.lwm_profile_count.restype = ctypes.c_int
+    L.lwm_profile_count.argtypes = []
+    L.lwm_profile_get.restype = ctypes.c_int
+    L.lwm_profile_get.argtypes = [I32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(F64), ctypes.POINTER(I64)]
     _lib = L
     return L
 
@@ -163,3 +172,22 @@ def lwm_ring_step(q, k_shard, v_shard, o_acc, lse_acc, seg_q=None, seg_k=None, q
                                _ptr(_seg(seg_k)), int(q_offset), int(k_offset), int(bool(causal)), float(scale),
                                _ref(tensor4(o_acc)), _ptr(lse_acc), _ref(tensor4(o_final)), _stream(q)))
     return o_acc, lse_acc
+
+
+def lwm_profile_enable(on: bool = True):
+    _check(lib().lwm_profile_enable(int(bool(on))))
+
+
+def lwm_profile_reset():
+    _check(lib().lwm_profile_reset())
+
+
+def lwm_profile_read() -> dict:
+    """{kernel name: (total milliseconds, launches)} since the last reset (waits for the events)."""
+    L = lib()
+    out = {}
+    for i in range(L.lwm_profile_count()):
+        name, ms, n = ctypes.c_char_p(), ctypes.c_double(), ctypes.c_int64()
+        _check(L.lwm_profile_get(i, ctypes.byref(name), ctypes.byref(ms), ctypes.byref(n)))
+        out[name.value.decode()] = (ms.value, n.value)
+    return out

@@ -30,7 +30,9 @@ def bwd_case(B, Lq, Lk, H, seed, seg=None, q_offset=0, k_offset=0, causal=True):
         gg = host(g)
         assert np.all(np.isfinite(gg)), name
         if np.linalg.norm(r) == 0:
-            assert np.all(gg == 0), name
+            # e.g. a single visible key: dS = P (dP - delta) vanishes exactly; the GPU's dP and
+            # delta are float32 sums in different orders, so only rounding-level residue remains
+            assert np.max(np.abs(gg)) <= 1e-3, (name, float(np.max(np.abs(gg))))
             continue
         e = rel_fro(gg, r)
         out[name] = e
