@@ -77,7 +77,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
   const bool segs = p.seg_q != nullptr;
 
   int kbeg = 0, kend = p.Lk;
-  if (p.causal) kend = (int)max<int64_t>(0, min<int64_t>(kend, p.q_offset + qlast - p.k_offset + 1));
+  if (p.causal) kend = (int)imax64(0, imin64(kend, p.q_offset + qlast - p.k_offset + 1));
   if (segs) {
     int lo, hi;
     segment_range(p.seg_k + (int64_t)b * p.Lk, p.Lk, p.seg_q[(int64_t)b * p.Lq + q0], p.seg_q[(int64_t)b * p.Lq + qlast],
@@ -245,7 +245,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
 
   // queries that can see any key of this tile
   int qbeg = 0, qend = p.Lq;
-  if (p.causal) qbeg = (int)min<int64_t>(p.Lq, max<int64_t>(0, p.k_offset + k0 - p.q_offset));
+  if (p.causal) qbeg = (int)imin64(p.Lq, imax64(0, p.k_offset + k0 - p.q_offset));
   if (segs) {
     int lo, hi;
     segment_range(p.seg_q + (int64_t)b * p.Lq, p.Lq, p.seg_k[(int64_t)b * p.Lk + k0], p.seg_k[(int64_t)b * p.Lk + klast],

@@ -50,6 +50,65 @@ __device__ __forceinline__ void write_transposed_quad(u32x4* tile, int quad, int
   }
 }
 
+// ---------------------------------------------------------------- direct-to-LDS tiles (CDNA4)
+// A tile is R rows (keys or queries) x 128 bf16 features, row-major, one 256-byte row per key:
+// exactly one row of the 64 x 4-byte LDS banks.  The sixteen 16-byte chunks of row r are stored
+// at chunk c ^ swz16(r): the 16 rows read by one MFMA operand fetch (ds_read_b128) hit 16
+// distinct chunk slots, and so do the 4 rows x 4 chunks read by one 32-lane half of a
+// transposing read (ds_read_b64_tr_b16).
+__device__ __forceinline__ int swz16(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Buffer resource over [base, base + bytes): loads past the end return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = (int)imax64(0, imin64(bytes, 0x7fffffff));  // a scalar: base and size are uniform
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+// 16 bytes per lane from rsrc + voffset straight into LDS at lds_base + 16 * lane (the wave's
+// 1 KB block); no registers involved.  lds_base must be wave-uniform.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, void* lds_base, int voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, voffset, 0, 0, 0);
+}
+// 4 bytes per lane, LDS at lds_base + 4 * lane.
+__device__ __forceinline__ void load_lds4(__amdgpu_buffer_rsrc_t r, void* lds_base, int voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 4, voffset, 0, 0, 0);
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// MFMA A operand "X^T" (32 features x 16 rows of X) read from a row-major swizzled tile with two
+// transposing reads.  Lane l receives feature db*32 + l%32 of rows g*16 + 4*(l/32) + {0..3} and
+// g*16 + 8 + 4*(l/32) + {0..3}: the row order of a 32x32 accumulator's lane half, so the B operand
+// can be packed straight from accumulator registers.  `off` comes from tr_offsets().
+__device__ __forceinline__ bf16x8 read_xt(const uint8_t* tile, int off_lo, int off_hi) {
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + off_lo));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + off_hi));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+// Byte offsets (within a tile, group g = 0) of this lane's two transposing reads for feature
+// block db.  Within each 16-lane group, lane 4j + r points at row j, features 4r..4r+3 of its
+// group's slice, so that lane 4r + c receives feature 4r + c of rows j = 0..3.
+__device__ __forceinline__ void tr_offsets(int lane, int db, int& off_lo, int& off_hi) {
+  const int gp = lane >> 4, j = (lane >> 2) & 3, r = lane & 3;
+  const int col = db * 32 + 16 * (gp & 1) + 4 * r;  // first feature of this lane's 8 bytes
+  const int chunk = col >> 3, sub = (col & 7) * 2;
+  const int row_lo = 4 * (gp >> 1) + j, row_hi = row_lo + 8;
+  off_lo = row_lo * 256 + ((chunk ^ swz16(row_lo)) << 4) + sub;
+  off_hi = row_hi * 256 + ((chunk ^ swz16(row_hi)) << 4) + sub;
+}
+// Byte offset of the 16-byte chunk `c` of row `row` in a swizzled tile (ds_read_b128 operand).
+__device__ __forceinline__ int rm_offset(int row, int c) { return row * 256 + ((c ^ swz16(row & 15)) << 4); }
+
 // ---------------------------------------------------------------- workgroup order
 // Grid position -> (batch*head, tile).  `descending` numbers tiles from the last one (causal
 // forward: the longest query tiles first); otherwise from the first (backward over keys: the

@@ -33,11 +33,12 @@ namespace lwm {
 namespace {
 
 constexpr int BN = 64;                 // keys per tile (bf16 path)
+constexpr int kTileBytes = BN * 256;   // one K or V tile: 64 rows x 128 bf16
 constexpr float kRescaleSlack = 8.0f;  // log2 units: p <= 2^8 between rescales
 
+// Two stages of (K tile, V tile, 64 segment ids); 2 workgroups fit in one CU's LDS.
 struct SmemBf16 {
-  u32x4 k[2][BN * 16];        // [stage] row-major K tile, rm_index(key, chunk)
-  u32x4 vt[2][D * (BN / 8)];  // [stage] transposed V tile, t64_index(feature, chunk)
+  uint8_t kv[2][2][kTileBytes];
   int32_t seg[2][BN];
 };
 static_assert(sizeof(SmemBf16) <= 80 * 1024, "two workgroups per CU must fit in LDS");
@@ -49,7 +50,7 @@ __device__ inline void key_range(const FwdParams& p, int b, int r0, int r1, int&
   kend = p.Lk;
   if (p.causal) {
     const int64_t lim = p.q_offset + r1 - p.k_offset + 1;
-    kend = (int)max<int64_t>(0, min<int64_t>(kend, lim));
+    kend = (int)imax64(0, imin64(kend, lim));
   }
   if (p.seg_q) {
     int lo, hi;
@@ -61,13 +62,17 @@ __device__ inline void key_range(const FwdParams& p, int b, int r0, int r1, int&
 }
 
 // ---------------------------------------------------------------------------- bf16 kernel
+// Streams K/V tiles HBM -> LDS with buffer loads that write LDS directly (no staging registers,
+// no per-tile address arithmetic beyond a scalar tile base; rows past the end read as zero).
+// The swizzle of a tile is chosen by the source address each lane loads.
 template <int QB>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdParams p) {
   constexpr int MW = 32 * QB;
   constexpr int BM = kWaves * MW;
-  __shared__ SmemBf16 sm;
+  __shared__ __attribute__((aligned(1024))) SmemBf16 sm;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // the wave index is uniform; say so, so LDS bases derived from it stay in scalar registers
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c32 = lane & 31, h32 = lane >> 5;
   const int nqt = (p.Lq + BM - 1) / BM;
   int bh, qt;
@@ -81,7 +86,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdParams p)
   const int t_begin = kbeg / BN;
   const int ntiles = (kend > kbeg) ? (kend + BN - 1) / BN - t_begin : 0;
 
-  // this wave's rows and their visibility bounds
   const int wr0 = q0 + w * MW;
   const int wr1 = min(wr0 + MW, p.Lq) - 1;  // may be < wr0 for a ragged last tile
   const bool wave_rows = wr1 >= wr0;
@@ -93,8 +97,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdParams p)
   }
 
   const uint16_t* __restrict__ qg = static_cast<const uint16_t*>(p.q) + b * p.sq.b + hh * p.sq.h;
-  const uint16_t* __restrict__ kg = static_cast<const uint16_t*>(p.k) + b * p.sk.b + hh * p.sk.h;
-  const uint16_t* __restrict__ vg = static_cast<const uint16_t*>(p.v) + b * p.sv.b + hh * p.sv.h;
+  const uint8_t* kg = reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(p.k) + b * p.sk.b + hh * p.sk.h);
+  const uint8_t* vg = reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(p.v) + b * p.sv.b + hh * p.sv.h);
+  const int64_t kl_bytes = p.sk.l * 2, vl_bytes = p.sv.l * 2;
+  const int64_t k_extent = (int64_t)(p.Lk - 1) * kl_bytes + 256, v_extent = (int64_t)(p.Lk - 1) * vl_bytes + 256;
+  const int32_t* segk_row = segs ? p.seg_k + (int64_t)b * p.Lk : nullptr;
 
   int qrow[QB];
   int64_t gq[QB];
@@ -142,46 +149,46 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdParams p)
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) m_init[qb] = m[qb];
 
-  // ---- register-staged K/V tile loader
-  u32x4 kst[4], vst[4];
-  int32_t segst = -1;
-  const int ld_key = tid >> 4, ld_c = tid & 15;  // K: 4 passes of 16 keys x 16 chunks
-  const int ld_kq = tid >> 4, ld_dg = tid & 15;  // V: key quad x feature chunk
-  auto gload = [&](int tile) {
+  // ---- per-lane load plan: wave w fills 1 KB blocks w*4 .. w*4+3 of each tile (4 rows per block);
+  // lane l of a block holds row 4*blk + l/16, physical chunk l%16 = logical chunk ^ swz16(row).
+  int ld_voff_k[4], ld_voff_v[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = (w * 4 + r) * 4 + (lane >> 4);
+    const int c = (lane & 15) ^ swz16(row);
+    ld_voff_k[r] = (int)(row * kl_bytes) + c * 16;
+    ld_voff_v[r] = (int)(row * vl_bytes) + c * 16;
+  }
+  auto issue = [&](int tile, int st) {
     const int k0 = tile * BN;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + k0 * kl_bytes, k_extent - k0 * kl_bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + k0 * vl_bytes, v_extent - k0 * vl_bytes);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int key = k0 + r * 16 + ld_key;
-      kst[r] = (key < p.Lk) ? *reinterpret_cast<const u32x4*>(kg + key * p.sk.l + ld_c * 8) : u32x4{0u, 0u, 0u, 0u};
+      load_lds16(rk, &sm.kv[st][0][(w * 4 + r) * 1024], ld_voff_k[r]);
+      load_lds16(rv, &sm.kv[st][1][(w * 4 + r) * 1024], ld_voff_v[r]);
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = k0 + 4 * ld_kq + r;
-      vst[r] = (key < p.Lk) ? *reinterpret_cast<const u32x4*>(vg + key * p.sv.l + ld_dg * 8) : u32x4{0u, 0u, 0u, 0u};
-    }
-    if (segs && tid < BN) segst = (k0 + tid < p.Lk) ? p.seg_k[(int64_t)b * p.Lk + k0 + tid] : -1;
-  };
-  auto swrite = [&](int st) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = r * 16 + ld_key;
-      sm.k[st][rm_index(key, ld_c)] = kst[r];
-    }
-    // V: 4 keys x 8 features -> feature-major
-    write_transposed_quad<BN>(sm.vt[st], ld_kq, ld_dg, vst);
-    if (segs && tid < BN) sm.seg[st][tid] = segst;
+    if (segs && w == 0) load_lds4(make_rsrc(segk_row + k0, (int64_t)(p.Lk - k0) * 4), &sm.seg[st][0], lane * 4);
   };
 
-  if (ntiles > 0) {
-    gload(t_begin);
-    swrite(0);
-    __syncthreads();
-  }
+  // ---- per-lane LDS read offsets (constant over tiles)
+  int koff[8];  // K operand for feature step sd: row c32 (+32 per key block), chunk 2*sd + h32
+#pragma unroll
+  for (int sd = 0; sd < 8; ++sd) koff[sd] = rm_offset(c32, 2 * sd + h32);
+  int vlo[4], vhi[4];  // V^T operand for feature block db (+4096 per 16-key group)
+#pragma unroll
+  for (int db = 0; db < 4; ++db) tr_offsets(lane, db, vlo[db], vhi[db]);
+
+  if (ntiles > 0) issue(t_begin, 0);
 
   for (int it = 0; it < ntiles; ++it) {
     const int st = it & 1;
     const int k0 = (t_begin + it) * BN;
-    if (it + 1 < ntiles) gload(t_begin + it + 1);
+    wait_vmcnt<0>();   // this wave's loads of tile `it` have landed in LDS
+    __syncthreads();   // ... and every other wave's; everyone is done with tile it-1
+    if (it + 1 < ntiles) issue(t_begin + it + 1, st ^ 1);
+    const uint8_t* kt = sm.kv[st][0];
+    const uint8_t* vt = sm.kv[st][1];
 
     // does this wave see any key of the tile, and does it need the element mask?
     bool active = wave_rows;
@@ -195,119 +202,127 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdParams p)
       active = active && !(ts1 < wseg0 || ts0 > wseg1);
       need_mask = need_mask || !(ts0 == ts1 && wseg0 == wseg1 && ts0 == wseg0);
     }
+    if (!active) continue;
 
-    if (active) {
-      // ---- S^T = K Q^T: [2 key blocks][QB query blocks] of 32x32
-      f32x16 s[2][QB];
+    // ---- S^T = K Q^T: [2 key blocks][QB query blocks] of 32x32.  K fragments are read two
+    // feature steps ahead of the MFMAs that consume them (scheduling barriers keep the order).
+    f32x16 s[2][QB];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) s[kb][qb][i] = 0.f;
+        for (int i = 0; i < 16; ++i) s[kb][qb][i] = 0.f;
+    {
+      bf16x8 kf[3][2];
+      auto kread = [&](int sd, bf16x8 (&dst)[2]) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) dst[kb] = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + kb * 8192 + koff[sd]));
+      };
+      kread(0, kf[0]);
+      kread(1, kf[1]);
 #pragma unroll
       for (int sd = 0; sd < 8; ++sd) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int key = kb * 32 + c32;
-          const int chunk = 2 * sd + h32;
-          const bf16x8 a = as_bf16x8(sm.k[st][rm_index(key, chunk)]);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma_32x32x16(a, qreg[qb][sd], s[kb][qb]);
-        }
-      }
-
-      if (need_mask) {
+        if (sd + 2 < 8) kread(sd + 2, kf[(sd + 2) % 3]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int kl = kb * 32 + acc_row(i, h32);
-            const int key = k0 + kl;
-            const bool in_range = key < p.Lk;
-            const int32_t ks = segs ? sm.seg[st][kl] : 0;
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-              bool vis = in_range;
-              if (p.causal) vis = vis && (p.k_offset + key <= gq[qb]);
-              if (segs) vis = vis && (ks == myseg[qb]);
-              if (!vis) s[kb][qb][i] = -INFINITY;
-            }
-          }
+          for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma_32x32x16(kf[sd % 3][kb], qreg[qb][sd], s[kb][qb]);
+        __builtin_amdgcn_sched_barrier(0);
       }
+    }
 
-      // ---- online softmax (log2 domain), lazily rescaled
-      float mx[QB];
-      bool need_rescale = false;
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float v = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) v = fmaxf(v, s[kb][qb][i]);
-        v = fmaxf(v, swap_halves(v));
-        mx[qb] = v * p.scale_log2;
-        need_rescale = need_rescale || (mx[qb] > m[qb] + kRescaleSlack);
-      }
-      if (__any(need_rescale)) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const float mnew = fmaxf(m[qb], mx[qb]);
-          const float alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(m[qb] - mnew);
-#pragma unroll
-          for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[qb][db][i] *= alpha;
-          l[qb] *= alpha;
-          m[qb] = mnew;
-        }
-      }
-
-      // p = exp2(s * scale_log2 - m), rounded to bf16; l += sum of the rounded values
-      bf16x8 pb[2][2][QB];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const float moff = (m[qb] == -INFINITY) ? 0.f : m[qb];
-        float lsum = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            u32x4 packed;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float e0 = fast_exp2(__builtin_fmaf(s[kb][qb][u * 8 + 2 * j], p.scale_log2, -moff));
-              const float e1 = fast_exp2(__builtin_fmaf(s[kb][qb][u * 8 + 2 * j + 1], p.scale_log2, -moff));
-              const uint32_t word = pack_bf16x2(e0, e1);
-              lsum = sum_bf16x2(word, lsum);
-              packed[j] = word;
-            }
-            pb[kb][u][qb] = as_bf16x8(packed);
-          }
-        l[qb] += lsum;
-      }
-
-      // ---- O^T += V^T P^T
+    if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int g = kb * 2 + u;
+        for (int i = 0; i < 16; ++i) {
+          const int kl = kb * 32 + acc_row(i, h32);
+          const int key = k0 + kl;
+          const bool in_range = key < p.Lk;
+          const int32_t ks = segs ? sm.seg[st][kl] : 0;
 #pragma unroll
-          for (int db = 0; db < 4; ++db) {
-            const int d = db * 32 + c32;
-            const int chunk = g * 2 + h32;
-            const bf16x8 a = as_bf16x8(sm.vt[st][t64_index(d, chunk)]);
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma_32x32x16(a, pb[kb][u][qb], acc[qb][db]);
+          for (int qb = 0; qb < QB; ++qb) {
+            bool vis = in_range;
+            if (p.causal) vis = vis && (p.k_offset + key <= gq[qb]);
+            if (segs) vis = vis && (ks == myseg[qb]);
+            if (!vis) s[kb][qb][i] = -INFINITY;
           }
         }
     }
 
-    if (it + 1 < ntiles) swrite(st ^ 1);
-    __syncthreads();
+    // ---- online softmax (log2 domain), lazily rescaled
+    float mx[QB];
+    bool need_rescale = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float v = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v = fmaxf(v, s[kb][qb][i]);
+      v = fmaxf(v, swap_halves(v));
+      mx[qb] = v * p.scale_log2;
+      need_rescale = need_rescale || (mx[qb] > m[qb] + kRescaleSlack);
+    }
+    if (__any(need_rescale)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float mnew = fmaxf(m[qb], mx[qb]);
+        const float alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(m[qb] - mnew);
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[qb][db][i] *= alpha;
+        l[qb] *= alpha;
+        m[qb] = mnew;
+      }
+    }
+
+    // p = exp2(s * scale_log2 - m), rounded to bf16; l += sum of the rounded values
+    bf16x8 pb[2][2][QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float moff = (m[qb] == -INFINITY) ? 0.f : m[qb];
+      float lsum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          u32x4 packed;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float e0 = fast_exp2(__builtin_fmaf(s[kb][qb][u * 8 + 2 * j], p.scale_log2, -moff));
+            const float e1 = fast_exp2(__builtin_fmaf(s[kb][qb][u * 8 + 2 * j + 1], p.scale_log2, -moff));
+            const uint32_t word = pack_bf16x2(e0, e1);
+            lsum = sum_bf16x2(word, lsum);
+            packed[j] = word;
+          }
+          pb[kb][u][qb] = as_bf16x8(packed);
+        }
+      l[qb] += lsum;
+    }
+
+    // ---- O^T += V^T P^T (V^T operands by transposing reads of the row-major V tile, issued
+    // two operands ahead of their MFMAs)
+    {
+      bf16x8 vf[3];
+      auto vread = [&](int n) { return read_xt(vt + (n >> 2) * 4096, vlo[n & 3], vhi[n & 3]); };
+      vf[0] = vread(0);
+      vf[1] = vread(1);
+#pragma unroll
+      for (int n = 0; n < 16; ++n) {  // n = 16-key group * 4 + feature block
+        if (n + 2 < 16) vf[(n + 2) % 3] = vread(n + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        const int g = n >> 2, db = n & 3;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma_32x32x16(vf[n % 3], pb[g >> 1][g & 1][qb], acc[qb][db]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   }
+  __syncthreads();  // all waves are done reading tiles before the epilogue reuses the LDS
 
   // ---- epilogue: O = acc / l, lse = (m + log2 l) ln 2
   uint16_t* og = static_cast<uint16_t*>(p.o);

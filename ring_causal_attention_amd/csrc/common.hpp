@@ -64,6 +64,10 @@ __device__ __forceinline__ float swap_halves(float x) {
   return __shfl_xor(x, 32, kWave);
 }
 
+// Integer min / max for 64-bit values (the generic overloads may go through double).
+__device__ __forceinline__ int64_t imin64(int64_t a, int64_t b) { return a < b ? a : b; }
+__device__ __forceinline__ int64_t imax64(int64_t a, int64_t b) { return a > b ? a : b; }
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

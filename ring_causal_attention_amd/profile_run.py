@@ -1,0 +1,121 @@
+"""Driver for rocprofv3 runs of the hot path, and the summariser of their counter output.
+
+Run under the profiler (one counter pass per run, e.g. ``--pmc FETCH_SIZE``):
+
+    rocprofv3 --pmc FETCH_SIZE -d OUT -o fetch -- python3 -m ring_causal_attention_amd.profile_run \
+        --workload train_step_L32768 --steps 2
+
+``--copy-mib N`` instead runs a plain device-to-device copy of N MiB (torch ``copy_``), whose
+FETCH_SIZE / WRITE_SIZE give the factor that turns the counters into bytes.
+
+``--summarize DIR`` reads the ``*_counter_collection.csv`` files under DIR and writes
+``profiles/traffic_<workload>.json`` (HBM bytes per launch of each kernel, scaled by the copy
+calibration, tagged with the digest of the kernel sources) plus a Markdown table on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import json
+import os
+import sys
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def run_workload(name: str, steps: int):
+    import torch
+    from . import configs, lwm, path, workloads
+    w = configs.WORKLOADS[name]
+    d = workloads.device_inputs(workloads.host_inputs(w))
+    if w.backward:
+        bufs = path.TrainStepBuffers(d["q"], d["k"])
+        step = lambda: path.training_step(d["q"], d["k"], d["v"], d["do"], w.theta, buffers=bufs)
+    elif w.ring_shards:
+        S = w.Lq
+        qr = lwm.lwm_rope_apply(d["q"], pos_offset=w.q_offset, theta=w.theta)
+        kr = {j: lwm.lwm_rope_apply(x, pos_offset=j * S, theta=w.theta) for j, x in d["k_shards"].items()}
+        step = lambda: path.ring_forward(qr, kr, d["v_shards"], w.ring_order(), S, w.q_offset)
+    else:
+        step = lambda: path.attention_forward(d["q"], d["k"], d["v"], w.theta, seg=d["seg"])
+    for i in range(steps):
+        step()
+        torch.cuda.synchronize()
+        print(f"[profile_run] {name} step {i + 1}/{steps} done", flush=True)
+
+
+def run_copy(mib: int):
+    import torch
+    n = mib * (1 << 20) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(f"[profile_run] copied {mib} MiB three times", flush=True)
+
+
+def _short(kernel_name: str) -> str:
+    for key in ("bwd_dkdv", "bwd_dq", "bwd_delta", "attn_fwd_bf16", "attn_fwd_f32", "rope_kernel"):
+        if key in kernel_name:
+            return key
+    return kernel_name.split("(")[0][-60:]
+
+
+def summarize(directory: str, workload: str, copy_mib: int):
+    """Average per dispatch of every counter, per kernel; bytes scaled by the copy calibration."""
+    vals = defaultdict(lambda: defaultdict(list))
+    for f in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                k = _short(row.get("Kernel_Name", ""))
+                vals[k][row["Counter_Name"]].append(float(row["Counter_Value"]))
+    avg = {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in vals.items()}
+    copy_key = next((k for k in avg if "copy" in k.lower() or "elementwise" in k.lower()), None)
+    out = {"workload": workload, "counters": avg}
+    if copy_key:
+        nbytes = copy_mib * (1 << 20)
+        fr = avg[copy_key].get("FETCH_SIZE")
+        fw = avg[copy_key].get("WRITE_SIZE")
+        out["calibration"] = {"copy_kernel": copy_key, "bytes": nbytes,
+                              "fetch_kib_per_byte": fr / nbytes if fr else None,
+                              "write_kib_per_byte": fw / nbytes if fw else None}
+        kern = {}
+        for k, cs in avg.items():
+            if k == copy_key:
+                continue
+            rb = cs.get("FETCH_SIZE") / (fr / nbytes) if fr and "FETCH_SIZE" in cs else None
+            wb = cs.get("WRITE_SIZE") / (fw / nbytes) if fw and "WRITE_SIZE" in cs else None
+            if rb is not None or wb is not None:
+                kern[k] = {"read_bytes": rb, "write_bytes": wb, "bytes_per_launch": (rb or 0) + (wb or 0)}
+        out["kernels"] = kern
+    from .build import sources_digest
+    out["sources_sha"] = sources_digest()
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workload", default="train_step_L32768")
+    ap.add_argument("--steps", type=int, default=2)
+    ap.add_argument("--copy-mib", type=int, default=0)
+    ap.add_argument("--summarize", default=None)
+    ap.add_argument("--write", action="store_true", help="write profiles/traffic_<workload>.json")
+    args = ap.parse_args()
+    if args.summarize:
+        res = summarize(args.summarize, args.workload, args.copy_mib or 1024)
+        if args.write:
+            with open(os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json"), "w") as f:
+                json.dump(res, f, indent=1)
+        print(json.dumps(res, indent=1))
+        return
+    if args.copy_mib:
+        run_copy(args.copy_mib)
+    else:
+        run_workload(args.workload, args.steps)
+
+
+if __name__ == "__main__":
+    sys.exit(main())
