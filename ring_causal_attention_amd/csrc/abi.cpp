@@ -46,6 +46,8 @@ int check_tensor(const lwm_tensor4* t, const char* name) {
   if (t->sB % vec || t->sL % vec || t->sH % vec)
     return fail(LWM_ERR_INVALID_ARG, "%s: strides must be multiples of %lld elements (16 bytes)", name, (long long)vec);
   if (t->sB < 0 || t->sL < 0 || t->sH < 0) return fail(LWM_ERR_INVALID_ARG, "%s: negative stride", name);
+  if (t->sL * (int64_t)elem_size(t->dtype) >= (int64_t(1) << 24))
+    return fail(LWM_ERR_UNSUPPORTED, "%s: row stride of 16 MiB or more (tiles use 32-bit offsets)", name);
   const bool empty = t->B == 0 || t->L == 0 || t->H == 0;
   if (!empty) {
     if (!t->ptr) return fail(LWM_ERR_INVALID_ARG, "%s: data pointer is NULL", name);
@@ -152,8 +154,8 @@ size_t lwm_blockattn_bwd_workspace_size(int64_t B, int64_t H, int64_t Lq, int64_
   (void)Lk;
   (void)D;
   if (B <= 0 || H <= 0 || Lq <= 0) return 256;
-  const size_t delta = (size_t)B * (size_t)H * (size_t)Lq * sizeof(float);
-  return (delta + 255) / 256 * 256;
+  const size_t rows = (size_t)B * (size_t)H * (size_t)Lq * sizeof(float);
+  return 2 * ((rows + 255) / 256 * 256);  // delta, then lse * log2(e)
 }
 
 int lwm_blockattn_bwd(const lwm_tensor4* q, const lwm_tensor4* k, const lwm_tensor4* v, const lwm_tensor4* o,
@@ -186,6 +188,7 @@ int lwm_blockattn_bwd(const lwm_tensor4* q, const lwm_tensor4* k, const lwm_tens
   p.sq = strides(q); p.sk = strides(k); p.sv = strides(v); p.so = strides(o); p.sdo = strides(dout);
   p.lse = lse;
   p.delta = static_cast<float*>(workspace);
+  p.lse2 = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) + need / 2) : nullptr;
   p.B = (int)q->B; p.H = (int)q->H; p.Lq = (int)q->L; p.Lk = (int)k->L;
   p.seg_q = seg_q; p.seg_k = seg_k;
   p.q_offset = q_offset; p.k_offset = k_offset; p.causal = causal;

@@ -8,30 +8,25 @@
 //     dV = P^T dO,   dP = dO V^T,   dS = P o (dP - delta),   dQ = scale dS K,   dK = scale dS^T Q.
 //
 // Three kernels, no atomics (the result is deterministic):
-//  * delta: one pass over dO and O (HBM-bound).
+//  * delta: one pass over dO and O (HBM-bound); also stores lse * log2(e) for the other two.
 //  * dQ: a workgroup per 128-query tile walks the visible 64-key tiles like the forward does,
-//    with scores transposed (S^T = K Q^T) so each lane owns one query: P^T and dS^T are formed
-//    in registers and feed dQ^T += K^T dS^T directly (K is staged both row-major and transposed).
-//  * dK/dV: a workgroup per 128-key tile (32 keys per wave) walks the visible 32-query tiles with
+//    with scores transposed (S^T = K Q^T) so each lane owns one query: P^T and dS^T are formed in
+//    registers and feed dQ^T += K^T dS^T directly; K^T operands come from the row-major K tile by
+//    transposing LDS reads.
+//  * dK/dV: a workgroup per 128-key tile (32 keys per wave) walks the visible 64-query tiles with
 //    scores in the other orientation (S = Q K^T, each lane owns one key): P and dS feed
-//    dV^T += dO^T P and dK^T += Q^T dS directly (Q and dO are staged both row-major and transposed).
-//  Recomputing S and dP in both kernels costs two extra products over the five the method needs;
-//  in exchange no partial dQ is ever written to or reduced through memory.
+//    dV^T += dO^T P and dK^T += Q^T dS directly; Q^T and dO^T operands come from the row-major tiles
+//    by transposing LDS reads.
+//  Tiles travel HBM -> LDS by buffer loads that write LDS directly (double-buffered).  Recomputing
+//  S and dP in both kernels costs two extra products over the five the method needs; in exchange
+//  no partial dQ is ever written to or reduced through memory.
 #include "attn_common.hpp"
 #include "profile.hpp"
 
 namespace lwm {
 namespace {
 
-constexpr int BNQ = 64;  // keys per tile in the dQ kernel
-constexpr int BQK = 32;  // queries per tile in the dK/dV kernel
-
-__device__ __forceinline__ float lse_log2(const float* lse_row, int q, int Lq) {
-  // +inf for rows without any visible key or past the end: exp2(s - inf) = 0 for every s
-  if (q >= Lq) return INFINITY;
-  const float v = lse_row[q];
-  return v == -INFINITY ? INFINITY : v * kLog2e;
-}
+constexpr int kTileBytes = 64 * 256;  // 64 rows x 128 bf16
 
 // ------------------------------------------------------------------------------ delta
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
@@ -52,21 +47,26 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
   }
 #pragma unroll
   for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
-  if (r < rows && c == 0) p.delta[((int64_t)b * p.H + h) * p.Lq + i] = acc;
+  if (r < rows && c == 0) {
+    const int64_t at = ((int64_t)b * p.H + h) * p.Lq + i;
+    p.delta[at] = acc;
+    // rows without any visible key: +inf makes exp2(s - lse2) = 0 for every score
+    const float ls = p.lse[at];
+    p.lse2[at] = ls == -INFINITY ? INFINITY : ls * kLog2e;
+  }
 }
 
 // ------------------------------------------------------------------------------ dQ
 struct SmemDq {
-  u32x4 k[2][BNQ * 16];       // row-major K, rm_index
-  u32x4 kt[2][D * (BNQ / 8)]; // transposed K, t64_index
-  u32x4 v[2][BNQ * 16];       // row-major V, rm_index
-  int32_t seg[2][BNQ];
+  uint8_t kv[2][2][kTileBytes];  // [stage][K, V] row-major swizzled
+  int32_t seg[2][64];
 };
+static_assert(sizeof(SmemDq) >= kWaves * 32 * D * 2, "epilogue staging must fit");
 
-__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
-  constexpr int MW = 32, BM = kWaves * MW;
-  __shared__ SmemDq sm;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
+  constexpr int MW = 32, BM = kWaves * MW, BN = 64;
+  __shared__ __attribute__((aligned(1024))) SmemDq sm;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c32 = lane & 31, h32 = lane >> 5;
   const int nqt = (p.Lq + BM - 1) / BM;
   int bh, qt;
@@ -85,8 +85,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
     kbeg = max(kbeg, lo);
     kend = min(kend, hi);
   }
-  const int t_begin = kbeg / BNQ;
-  const int ntiles = (kend > kbeg) ? (kend + BNQ - 1) / BNQ - t_begin : 0;
+  const int t_begin = kbeg / BN;
+  const int ntiles = (kend > kbeg) ? (kend + BN - 1) / BN - t_begin : 0;
 
   const int wr0 = q0 + w * MW, wr1 = min(wr0 + MW, p.Lq) - 1;
   const bool wave_rows = wr1 >= wr0;
@@ -98,8 +98,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
   const int qrow = wr0 + c32;
   const int64_t gq = p.q_offset + qrow;
   const int32_t myseg = segs ? p.seg_q[(int64_t)b * p.Lq + min(qrow, p.Lq - 1)] : 0;
-  const float lse2 = lse_log2(p.lse + ((int64_t)b * p.H + hh) * p.Lq, qrow, p.Lq);
-  const float dlt = qrow < p.Lq ? p.delta[((int64_t)b * p.H + hh) * p.Lq + qrow] : 0.f;
+  const int64_t row_at = ((int64_t)b * p.H + hh) * p.Lq + qrow;
+  const float lse2 = qrow < p.Lq ? p.lse2[row_at] : INFINITY;
+  const float dlt = qrow < p.Lq ? p.delta[row_at] : 0.f;
 
   bf16x8 qreg[8], doreg[8];
   {
@@ -122,118 +123,132 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
 
-  const uint16_t* kg = p.k + b * p.sk.b + hh * p.sk.h;
-  const uint16_t* vg = p.v + b * p.sv.b + hh * p.sv.h;
-  const int ld_q = tid >> 4, ld_c = tid & 15;
-  u32x4 kst[4], vst[4];
-  int32_t segst = -1;
-  auto gload = [&](int tile) {
-    const int k0 = tile * BNQ;
+  const uint8_t* kg = reinterpret_cast<const uint8_t*>(p.k + b * p.sk.b + hh * p.sk.h);
+  const uint8_t* vg = reinterpret_cast<const uint8_t*>(p.v + b * p.sv.b + hh * p.sv.h);
+  const int64_t kl_bytes = p.sk.l * 2, vl_bytes = p.sv.l * 2;
+  const int64_t k_extent = (int64_t)(p.Lk - 1) * kl_bytes + 256, v_extent = (int64_t)(p.Lk - 1) * vl_bytes + 256;
+  const int32_t* segk_row = segs ? p.seg_k + (int64_t)b * p.Lk : nullptr;
+  int ld_voff_k[4], ld_voff_v[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int kk = k0 + 4 * ld_q + r;  // K: quad ld_q, chunk ld_c
-      kst[r] = kk < p.Lk ? *reinterpret_cast<const u32x4*>(kg + kk * p.sk.l + ld_c * 8) : u32x4{0u, 0u, 0u, 0u};
-      const int kv = k0 + r * 16 + ld_q;  // V: row r*16 + ld_q, chunk ld_c
-      vst[r] = kv < p.Lk ? *reinterpret_cast<const u32x4*>(vg + kv * p.sv.l + ld_c * 8) : u32x4{0u, 0u, 0u, 0u};
-    }
-    if (segs && tid < BNQ) segst = (k0 + tid < p.Lk) ? p.seg_k[(int64_t)b * p.Lk + k0 + tid] : -1;
-  };
-  auto swrite = [&](int st) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      sm.k[st][rm_index(4 * ld_q + r, ld_c)] = kst[r];
-      sm.v[st][rm_index(r * 16 + ld_q, ld_c)] = vst[r];
-    }
-    write_transposed_quad<BNQ>(sm.kt[st], ld_q, ld_c, kst);
-    if (segs && tid < BNQ) sm.seg[st][tid] = segst;
-  };
-
-  if (ntiles > 0) {
-    gload(t_begin);
-    swrite(0);
-    __syncthreads();
+  for (int r = 0; r < 4; ++r) {
+    const int row = (w * 4 + r) * 4 + (lane >> 4);
+    const int c = (lane & 15) ^ swz16(row);
+    ld_voff_k[r] = (int)(row * kl_bytes) + c * 16;
+    ld_voff_v[r] = (int)(row * vl_bytes) + c * 16;
   }
+  auto issue = [&](int tile, int st) {
+    const int k0 = tile * BN;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + k0 * kl_bytes, k_extent - k0 * kl_bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + k0 * vl_bytes, v_extent - k0 * vl_bytes);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      load_lds16(rk, &sm.kv[st][0][(w * 4 + r) * 1024], ld_voff_k[r]);
+      load_lds16(rv, &sm.kv[st][1][(w * 4 + r) * 1024], ld_voff_v[r]);
+    }
+    if (segs && w == 0) load_lds4(make_rsrc(segk_row + k0, (int64_t)(p.Lk - k0) * 4), &sm.seg[st][0], lane * 4);
+  };
+  int roff[8];  // K / V row-major operand for feature step sd (+8192 for the second key block)
+#pragma unroll
+  for (int sd = 0; sd < 8; ++sd) roff[sd] = rm_offset(c32, 2 * sd + h32);
+  int tlo[4], thi[4];  // K^T operand for feature block db (+4096 per 16-key group)
+#pragma unroll
+  for (int db = 0; db < 4; ++db) tr_offsets(lane, db, tlo[db], thi[db]);
+
+  if (ntiles > 0) issue(t_begin, 0);
   for (int it = 0; it < ntiles; ++it) {
     const int st = it & 1;
-    const int k0 = (t_begin + it) * BNQ;
-    if (it + 1 < ntiles) gload(t_begin + it + 1);
+    const int k0 = (t_begin + it) * BN;
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (it + 1 < ntiles) issue(t_begin + it + 1, st ^ 1);
+    const uint8_t* kt = sm.kv[st][0];
+    const uint8_t* vt = sm.kv[st][1];
     bool active = wave_rows;
-    bool need_mask = (k0 + BNQ > p.Lk) || (k0 < kbeg) || (k0 + BNQ > kend);
+    bool need_mask = (k0 + BN > p.Lk) || (k0 < kbeg) || (k0 + BN > kend);
     if (p.causal) {
       active = active && (p.k_offset + k0 <= p.q_offset + wr1);
-      need_mask = need_mask || (p.k_offset + k0 + BNQ - 1 > p.q_offset + wr0);
+      need_mask = need_mask || (p.k_offset + k0 + BN - 1 > p.q_offset + wr0);
     }
     if (segs) {
-      const int32_t ts0 = sm.seg[st][0], ts1 = sm.seg[st][min(BNQ, p.Lk - k0) - 1];
+      const int32_t ts0 = sm.seg[st][0], ts1 = sm.seg[st][min(BN, p.Lk - k0) - 1];
       active = active && !(ts1 < wseg0 || ts0 > wseg1);
       need_mask = need_mask || !(ts0 == ts1 && wseg0 == wseg1 && ts0 == wseg0);
     }
-    if (active) {
-      f32x16 s[2], dp[2];
+    if (!active) continue;
+
+    // S^T = K Q^T and dP^T = V dO^T, one key block at a time; operands read one step ahead
+    bf16x8 dsb[2][2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 s, dp;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[kb][i] = dp[kb][i] = 0.f;
+      for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+      bf16x8 fk[2], fv[2];
+      fk[0] = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + kb * 8192 + roff[0]));
+      fv[0] = as_bf16x8(*reinterpret_cast<const u32x4*>(vt + kb * 8192 + roff[0]));
 #pragma unroll
-      for (int sd = 0; sd < 8; ++sd)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int idx = rm_index(kb * 32 + c32, 2 * sd + h32);
-          s[kb] = mfma_32x32x16(as_bf16x8(sm.k[st][idx]), qreg[sd], s[kb]);
-          dp[kb] = mfma_32x32x16(as_bf16x8(sm.v[st][idx]), doreg[sd], dp[kb]);
+      for (int sd = 0; sd < 8; ++sd) {
+        if (sd + 1 < 8) {
+          fk[(sd + 1) & 1] = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + kb * 8192 + roff[sd + 1]));
+          fv[(sd + 1) & 1] = as_bf16x8(*reinterpret_cast<const u32x4*>(vt + kb * 8192 + roff[sd + 1]));
         }
-      bf16x8 dsb[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kl = kb * 32 + acc_row(i, h32);
-          bool vis = true;
-          if (need_mask) {
-            const int key = k0 + kl;
-            vis = key < p.Lk;
-            if (p.causal) vis = vis && (p.k_offset + key <= gq);
-            if (segs) vis = vis && (sm.seg[st][kl] == myseg);
-          }
-          const float pr = vis ? fast_exp2(__builtin_fmaf(s[kb][i], p.scale_log2, -lse2)) : 0.f;
-          s[kb][i] = pr * (dp[kb][i] - dlt);
-        }
-        dsb[kb][0] = pack8(s[kb], 0);
-        dsb[kb][1] = pack8(s[kb], 1);
+        __builtin_amdgcn_sched_barrier(0);
+        s = mfma_32x32x16(fk[sd & 1], qreg[sd], s);
+        dp = mfma_32x32x16(fv[sd & 1], doreg[sd], dp);
+        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int db = 0; db < 4; ++db) {
-            const bf16x8 a = as_bf16x8(sm.kt[st][t64_index(db * 32 + c32, (kb * 2 + u) * 2 + h32)]);
-            acc[db] = mfma_32x32x16(a, dsb[kb][u], acc[db]);
-          }
+      for (int i = 0; i < 16; ++i) {
+        const int kl = kb * 32 + acc_row(i, h32);
+        bool vis = true;
+        if (need_mask) {
+          const int key = k0 + kl;
+          vis = key < p.Lk;
+          if (p.causal) vis = vis && (p.k_offset + key <= gq);
+          if (segs) vis = vis && (sm.seg[st][kl] == myseg);
+        }
+        const float pr = vis ? fast_exp2(__builtin_fmaf(s[i], p.scale_log2, -lse2)) : 0.f;
+        s[i] = pr * (dp[i] - dlt);
+      }
+      dsb[kb][0] = pack8(s, 0);
+      dsb[kb][1] = pack8(s, 1);
     }
-    if (it + 1 < ntiles) swrite(st ^ 1);
-    __syncthreads();
+    // dQ^T += K^T dS^T (K^T operands by transposing reads, two ahead)
+    {
+      bf16x8 kf[3];
+      auto kread = [&](int n) { return read_xt(kt + (n >> 2) * 4096, tlo[n & 3], thi[n & 3]); };
+      kf[0] = kread(0);
+      kf[1] = kread(1);
+#pragma unroll
+      for (int n = 0; n < 16; ++n) {  // n = 16-key group * 4 + feature block
+        if (n + 2 < 16) kf[(n + 2) % 3] = kread(n + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        const int g = n >> 2, db = n & 3;
+        acc[db] = mfma_32x32x16(kf[n % 3], dsb[g >> 1][g & 1], acc[db]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   }
+  __syncthreads();
   uint8_t* stage_w = reinterpret_cast<uint8_t*>(&sm) + w * (32 * D * 2);
   store_rows_bf16(stage_w, acc, p.scale, p.dq + b * p.sdq.b + hh * p.sdq.h + wr0 * p.sdq.l, p.sdq.l,
                   max(0, min(32, p.Lq - wr0)));
 }
 
 // ------------------------------------------------------------------------------ dK / dV
+constexpr int BQ = 64;  // queries per tile in the dK/dV kernel
 struct SmemDkdv {
-  u32x4 q[2][BQK * 16];        // row-major Q tile, rm_index
-  u32x4 qt[2][D * (BQK / 8)];  // transposed Q tile, t32_index
-  u32x4 o[2][BQK * 16];        // row-major dO tile
-  u32x4 ot[2][D * (BQK / 8)];  // transposed dO tile
-  float lse2[2][BQK];
-  float dlt[2][BQK];
-  int32_t seg[2][BQK];
+  uint8_t qo[2][2][kTileBytes];  // [stage][Q, dO] row-major swizzled
+  float lse2[2][BQ];
+  float dlt[2][BQ];
+  int32_t seg[2][BQ];
 };
+static_assert(sizeof(SmemDkdv) >= kWaves * 32 * D * 2, "epilogue staging must fit");
 
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int NW = 32, BK = kWaves * NW;
-  __shared__ SmemDkdv sm;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  __shared__ __attribute__((aligned(1024))) SmemDkdv sm;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c32 = lane & 31, h32 = lane >> 5;
   const int nkt = (p.Lk + BK - 1) / BK;
   int bh, kt;
@@ -253,8 +268,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
     qbeg = max(qbeg, lo);
     qend = min(qend, hi);
   }
-  const int t_begin = qbeg / BQK;
-  const int ntiles = (qend > qbeg) ? (qend + BQK - 1) / BQK - t_begin : 0;
+  const int t_begin = qbeg / BQ;
+  const int ntiles = (qend > qbeg) ? (qend + BQ - 1) / BQ - t_begin : 0;
 
   const int wk0 = k0 + w * NW, wk1 = min(wk0 + NW, p.Lk) - 1;
   const bool wave_keys = wk1 >= wk0;
@@ -269,14 +284,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
 
   bf16x8 kreg[8], vreg[8];
   {
-    const uint16_t* kg = p.k + b * p.sk.b + hh * p.sk.h + (int64_t)krow * p.sk.l;
-    const uint16_t* vg = p.v + b * p.sv.b + hh * p.sv.h + (int64_t)krow * p.sv.l;
+    const uint16_t* kgr = p.k + b * p.sk.b + hh * p.sk.h + (int64_t)krow * p.sk.l;
+    const uint16_t* vgr = p.v + b * p.sv.b + hh * p.sv.h + (int64_t)krow * p.sv.l;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
       if (krow < p.Lk) {
-        a = *reinterpret_cast<const u32x4*>(kg + s * 16 + h32 * 8);
-        c = *reinterpret_cast<const u32x4*>(vg + s * 16 + h32 * 8);
+        a = *reinterpret_cast<const u32x4*>(kgr + s * 16 + h32 * 8);
+        c = *reinterpret_cast<const u32x4*>(vgr + s * 16 + h32 * 8);
       }
       kreg[s] = as_bf16x8(a);
       vreg[s] = as_bf16x8(c);
@@ -288,78 +303,89 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) dk[db][i] = dv[db][i] = 0.f;
 
-  // loader: threads 0..127 stage Q, 128..255 stage dO; each holds one quad of rows x one chunk
-  const bool ld_do = tid >= 128;
-  const int ld_q = (tid >> 4) & 7, ld_c = tid & 15;
-  const uint16_t* src = ld_do ? p.dout + b * p.sdo.b + hh * p.sdo.h : p.q + b * p.sq.b + hh * p.sq.h;
-  const int64_t src_l = ld_do ? p.sdo.l : p.sq.l;
-  const float* lse_row = p.lse + ((int64_t)b * p.H + hh) * p.Lq;
+  const uint8_t* qg = reinterpret_cast<const uint8_t*>(p.q + b * p.sq.b + hh * p.sq.h);
+  const uint8_t* og = reinterpret_cast<const uint8_t*>(p.dout + b * p.sdo.b + hh * p.sdo.h);
+  const int64_t ql_bytes = p.sq.l * 2, ol_bytes = p.sdo.l * 2;
+  const int64_t q_extent = (int64_t)(p.Lq - 1) * ql_bytes + 256, o_extent = (int64_t)(p.Lq - 1) * ol_bytes + 256;
+  const float* lse2_row = p.lse2 + ((int64_t)b * p.H + hh) * p.Lq;
   const float* dlt_row = p.delta + ((int64_t)b * p.H + hh) * p.Lq;
-  u32x4 rst[4];
-  float l2st = 0.f, dst = 0.f;
-  int32_t segst = -1;
-  auto gload = [&](int tile) {
-    const int q0 = tile * BQK;
+  const int32_t* segq_row = segs ? p.seg_q + (int64_t)b * p.Lq : nullptr;
+  int ld_voff_q[4], ld_voff_o[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = (w * 4 + r) * 4 + (lane >> 4);
+    const int c = (lane & 15) ^ swz16(row);
+    ld_voff_q[r] = (int)(row * ql_bytes) + c * 16;
+    ld_voff_o[r] = (int)(row * ol_bytes) + c * 16;
+  }
+  auto issue = [&](int tile, int st) {
+    const int q0 = tile * BQ;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qg + q0 * ql_bytes, q_extent - q0 * ql_bytes);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(og + q0 * ol_bytes, o_extent - q0 * ol_bytes);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int qq = q0 + 4 * ld_q + r;
-      rst[r] = qq < p.Lq ? *reinterpret_cast<const u32x4*>(src + qq * src_l + ld_c * 8) : u32x4{0u, 0u, 0u, 0u};
+      load_lds16(rq, &sm.qo[st][0][(w * 4 + r) * 1024], ld_voff_q[r]);
+      load_lds16(ro, &sm.qo[st][1][(w * 4 + r) * 1024], ld_voff_o[r]);
     }
-    if (tid < BQK) {
-      const int qq = q0 + tid;
-      l2st = lse_log2(lse_row, qq, p.Lq);
-      dst = qq < p.Lq ? dlt_row[qq] : 0.f;
-      if (segs) segst = qq < p.Lq ? p.seg_q[(int64_t)b * p.Lq + qq] : -1;
-    }
+    const int64_t rem = (int64_t)(p.Lq - q0) * 4;
+    if (w == 0) load_lds4(make_rsrc(lse2_row + q0, rem), &sm.lse2[st][0], lane * 4);
+    if (w == 1) load_lds4(make_rsrc(dlt_row + q0, rem), &sm.dlt[st][0], lane * 4);
+    if (segs && w == 2) load_lds4(make_rsrc(segq_row + q0, rem), &sm.seg[st][0], lane * 4);
   };
-  auto swrite = [&](int st) {
-    u32x4* rm = ld_do ? sm.o[st] : sm.q[st];
-    u32x4* tr = ld_do ? sm.ot[st] : sm.qt[st];
+  int roff[8];  // Q / dO row-major operand for feature step sd (+8192 for the second query block)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) rm[rm_index(4 * ld_q + r, ld_c)] = rst[r];
-    write_transposed_quad<BQK>(tr, ld_q, ld_c, rst);
-    if (tid < BQK) {
-      sm.lse2[st][tid] = l2st;
-      sm.dlt[st][tid] = dst;
-      if (segs) sm.seg[st][tid] = segst;
-    }
-  };
+  for (int sd = 0; sd < 8; ++sd) roff[sd] = rm_offset(c32, 2 * sd + h32);
+  int tlo[4], thi[4];  // Q^T / dO^T operand for feature block db (+4096 per 16-query group)
+#pragma unroll
+  for (int db = 0; db < 4; ++db) tr_offsets(lane, db, tlo[db], thi[db]);
 
-  if (ntiles > 0) {
-    gload(t_begin);
-    swrite(0);
-    __syncthreads();
-  }
+  if (ntiles > 0) issue(t_begin, 0);
   for (int it = 0; it < ntiles; ++it) {
     const int st = it & 1;
-    const int q0 = (t_begin + it) * BQK;
-    if (it + 1 < ntiles) gload(t_begin + it + 1);
+    const int q0 = (t_begin + it) * BQ;
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (it + 1 < ntiles) issue(t_begin + it + 1, st ^ 1);
+    const uint8_t* qt = sm.qo[st][0];
+    const uint8_t* ot = sm.qo[st][1];
     bool active = wave_keys;
     bool need_mask = false;
     if (p.causal) {
-      active = active && (p.q_offset + q0 + BQK - 1 >= p.k_offset + wk0);
+      active = active && (p.q_offset + q0 + BQ - 1 >= p.k_offset + wk0);
       need_mask = p.k_offset + wk1 > p.q_offset + q0;
     }
     if (segs) {
-      const int32_t ts0 = sm.seg[st][0], ts1 = sm.seg[st][min(BQK, p.Lq - q0) - 1];
+      const int32_t ts0 = sm.seg[st][0], ts1 = sm.seg[st][min(BQ, p.Lq - q0) - 1];
       active = active && !(ts1 < wseg0 || ts0 > wseg1);
       need_mask = need_mask || !(ts0 == ts1 && wseg0 == wseg1 && ts0 == wseg0);
     }
-    if (active) {
+    if (!active) continue;
+
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys
       f32x16 s, dp;
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+      bf16x8 fq[2], fo[2];
+      fq[0] = as_bf16x8(*reinterpret_cast<const u32x4*>(qt + qb * 8192 + roff[0]));
+      fo[0] = as_bf16x8(*reinterpret_cast<const u32x4*>(ot + qb * 8192 + roff[0]));
 #pragma unroll
       for (int sd = 0; sd < 8; ++sd) {
-        const int idx = rm_index(c32, 2 * sd + h32);
-        s = mfma_32x32x16(as_bf16x8(sm.q[st][idx]), kreg[sd], s);
-        dp = mfma_32x32x16(as_bf16x8(sm.o[st][idx]), vreg[sd], dp);
+        if (sd + 1 < 8) {
+          fq[(sd + 1) & 1] = as_bf16x8(*reinterpret_cast<const u32x4*>(qt + qb * 8192 + roff[sd + 1]));
+          fo[(sd + 1) & 1] = as_bf16x8(*reinterpret_cast<const u32x4*>(ot + qb * 8192 + roff[sd + 1]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        s = mfma_32x32x16(fq[sd & 1], kreg[sd], s);
+        dp = mfma_32x32x16(fo[sd & 1], vreg[sd], dp);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // lane owns key krow; element i is query q0 + acc_row(i, h32)
+      // lane owns key krow; element i is query q0 + qb*32 + acc_row(i, h32)
       f32x16 pm, ds;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int r4 = 8 * g + 4 * h32;
+        const int r4 = qb * 32 + 8 * g + 4 * h32;
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse2[st][r4]);
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dlt[st][r4]);
 #pragma unroll
@@ -376,22 +402,32 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
           ds[i] = pr * (dp[i] - d4[j]);
         }
       }
+      const bf16x8 pb[2] = {pack8(pm, 0), pack8(pm, 1)};
+      const bf16x8 dsb[2] = {pack8(ds, 0), pack8(ds, 1)};
+      // dV^T += dO^T P, dK^T += Q^T dS (transposed operands read two ahead)
+      bf16x8 fo_t[3], fq_t[3];
+      auto tread = [&](const uint8_t* tile, int n) {
+        return read_xt(tile + (qb * 2 + (n >> 2)) * 4096, tlo[n & 3], thi[n & 3]);
+      };
+      fo_t[0] = tread(ot, 0);
+      fq_t[0] = tread(qt, 0);
+      fo_t[1] = tread(ot, 1);
+      fq_t[1] = tread(qt, 1);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const bf16x8 pb = pack8(pm, u);
-        const bf16x8 dsb = pack8(ds, u);
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const int ti = t32_index(db * 32 + c32, u * 2 + h32);
-          dv[db] = mfma_32x32x16(as_bf16x8(sm.ot[st][ti]), pb, dv[db]);
-          dk[db] = mfma_32x32x16(as_bf16x8(sm.qt[st][ti]), dsb, dk[db]);
+      for (int n = 0; n < 8; ++n) {  // n = 16-query group (within this block) * 4 + feature block
+        if (n + 2 < 8) {
+          fo_t[(n + 2) % 3] = tread(ot, n + 2);
+          fq_t[(n + 2) % 3] = tread(qt, n + 2);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        const int u = n >> 2, db = n & 3;
+        dv[db] = mfma_32x32x16(fo_t[n % 3], pb[u], dv[db]);
+        dk[db] = mfma_32x32x16(fq_t[n % 3], dsb[u], dk[db]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (it + 1 < ntiles) swrite(st ^ 1);
-    __syncthreads();
   }
-  static_assert(sizeof(SmemDkdv) >= kWaves * 32 * D * 2, "epilogue staging must fit");
+  __syncthreads();
   uint8_t* stage_w = reinterpret_cast<uint8_t*>(&sm) + w * (32 * D * 2);
   const int rows_valid = max(0, min(32, p.Lk - wk0));
   store_rows_bf16(stage_w, dk, p.scale, p.dk + b * p.sdk.b + hh * p.sdk.h + wk0 * p.sdk.l, p.sdk.l, rows_valid);

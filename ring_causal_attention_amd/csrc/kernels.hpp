@@ -59,6 +59,7 @@ struct BwdParams {
   Strides sq, sk, sv, so, sdo;
   const float* lse;
   float* delta;  // workspace [B, H, Lq]: rowsum(dout * o)
+  float* lse2;   // workspace [B, H, Lq]: lse * log2(e), +inf where lse = -inf
   int B, H, Lq, Lk;
   const int32_t* seg_q;
   const int32_t* seg_k;
