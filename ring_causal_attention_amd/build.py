@@ -35,10 +35,17 @@ def hipcc() -> str:
     return h
 
 
+# Per-source code-generation options.  The backward's dK/dV kernel keeps 128 fp32 accumulators
+# live across its loop; with MFMA results in VGPRs the register allocator spills rarely used values
+# to AGPRs instead of copying the accumulators between the two files every iteration.
+SOURCE_FLAGS = {"attn_bwd.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str, extra=()) -> str:
     os.makedirs(BUILD, exist_ok=True)
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), *extra, "-I", os.path.join(ROOT, "include"), "-c",
+           os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -197,19 +197,22 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
         dp = mfma_32x32x16(fv[sd & 1], doreg[sd], dp);
         __builtin_amdgcn_sched_barrier(0);
       }
+      // masked scores get exponent -inf (a select, not a branch): exp2(-inf) = 0
+      float x[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int kl = kb * 32 + acc_row(i, h32);
-        bool vis = true;
-        if (need_mask) {
+      for (int i = 0; i < 16; ++i) x[i] = __builtin_fmaf(s[i], p.scale_log2, -lse2);
+      if (need_mask) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kl = kb * 32 + acc_row(i, h32);
           const int key = k0 + kl;
-          vis = key < p.Lk;
-          if (p.causal) vis = vis && (p.k_offset + key <= gq);
-          if (segs) vis = vis && (sm.seg[st][kl] == myseg);
+          const int32_t ks = segs ? sm.seg[st][kl] : myseg;
+          const bool vis = (key < p.Lk) & (!p.causal | (p.k_offset + key <= gq)) & (ks == myseg);
+          x[i] = vis ? x[i] : -INFINITY;
         }
-        const float pr = vis ? fast_exp2(__builtin_fmaf(s[i], p.scale_log2, -lse2)) : 0.f;
-        s[i] = pr * (dp[i] - dlt);
       }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = fast_exp2(x[i]) * (dp[i] - dlt);
       dsb[kb][0] = pack8(s, 0);
       dsb[kb][1] = pack8(s, 1);
     }
@@ -239,6 +242,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
 constexpr int BQ = 64;  // queries per tile in the dK/dV kernel
 struct SmemDkdv {
   uint8_t qo[2][2][kTileBytes];  // [stage][Q, dO] row-major swizzled
+  uint8_t kv[2][2 * kTileBytes]; // [K, V] of the workgroup's 128 keys (loaded once), row-major swizzled
   float lse2[2][BQ];
   float dlt[2][BQ];
   int32_t seg[2][BQ];
@@ -282,21 +286,24 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
   const int64_t gk = p.k_offset + krow;
   const int32_t myseg = segs ? p.seg_k[(int64_t)b * p.Lk + min(krow, p.Lk - 1)] : 0;
 
-  bf16x8 kreg[8], vreg[8];
+  // the workgroup's K and V (128 keys each) go to LDS once; each wave reads its 32 keys' operands
   {
-    const uint16_t* kgr = p.k + b * p.sk.b + hh * p.sk.h + (int64_t)krow * p.sk.l;
-    const uint16_t* vgr = p.v + b * p.sv.b + hh * p.sv.h + (int64_t)krow * p.sv.l;
+    const uint8_t* kgb = reinterpret_cast<const uint8_t*>(p.k + b * p.sk.b + hh * p.sk.h);
+    const uint8_t* vgb = reinterpret_cast<const uint8_t*>(p.v + b * p.sv.b + hh * p.sv.h);
+    const int64_t klb = p.sk.l * 2, vlb = p.sv.l * 2;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kgb + k0 * klb, (int64_t)(p.Lk - 1 - k0) * klb + 256);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vgb + k0 * vlb, (int64_t)(p.Lk - 1 - k0) * vlb + 256);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
-      if (krow < p.Lk) {
-        a = *reinterpret_cast<const u32x4*>(kgr + s * 16 + h32 * 8);
-        c = *reinterpret_cast<const u32x4*>(vgr + s * 16 + h32 * 8);
-      }
-      kreg[s] = as_bf16x8(a);
-      vreg[s] = as_bf16x8(c);
+    for (int r = 0; r < 8; ++r) {  // 32 blocks of 1 KB per tensor, 8 per wave
+      const int blk = w * 8 + r;
+      const int row = blk * 4 + (lane >> 4);
+      const int c = (lane & 15) ^ swz16(row);
+      load_lds16(rk, &sm.kv[0][blk * 1024], (int)(row * klb) + c * 16);
+      load_lds16(rv, &sm.kv[1][blk * 1024], (int)(row * vlb) + c * 16);
     }
   }
+  const uint8_t* kw = sm.kv[0] + w * 8192;  // this wave's 32 keys
+  const uint8_t* vw = sm.kv[1] + w * 8192;
   f32x16 dk[4], dv[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
@@ -367,22 +374,26 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
       f32x16 s, dp;
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
-      bf16x8 fq[2], fo[2];
-      fq[0] = as_bf16x8(*reinterpret_cast<const u32x4*>(qt + qb * 8192 + roff[0]));
-      fo[0] = as_bf16x8(*reinterpret_cast<const u32x4*>(ot + qb * 8192 + roff[0]));
+      // operands (Q, K, dO, V rows; the same lane layout) read one feature step ahead
+      bf16x8 f[2][4];
+      auto fread = [&](int sd, bf16x8 (&dst)[4]) {
+        dst[0] = as_bf16x8(*reinterpret_cast<const u32x4*>(qt + qb * 8192 + roff[sd]));
+        dst[1] = as_bf16x8(*reinterpret_cast<const u32x4*>(kw + roff[sd]));
+        dst[2] = as_bf16x8(*reinterpret_cast<const u32x4*>(ot + qb * 8192 + roff[sd]));
+        dst[3] = as_bf16x8(*reinterpret_cast<const u32x4*>(vw + roff[sd]));
+      };
+      fread(0, f[0]);
 #pragma unroll
       for (int sd = 0; sd < 8; ++sd) {
-        if (sd + 1 < 8) {
-          fq[(sd + 1) & 1] = as_bf16x8(*reinterpret_cast<const u32x4*>(qt + qb * 8192 + roff[sd + 1]));
-          fo[(sd + 1) & 1] = as_bf16x8(*reinterpret_cast<const u32x4*>(ot + qb * 8192 + roff[sd + 1]));
-        }
+        if (sd + 1 < 8) fread(sd + 1, f[(sd + 1) & 1]);
         __builtin_amdgcn_sched_barrier(0);
-        s = mfma_32x32x16(fq[sd & 1], kreg[sd], s);
-        dp = mfma_32x32x16(fo[sd & 1], vreg[sd], dp);
+        s = mfma_32x32x16(f[sd & 1][0], f[sd & 1][1], s);
+        dp = mfma_32x32x16(f[sd & 1][2], f[sd & 1][3], dp);
         __builtin_amdgcn_sched_barrier(0);
       }
       // lane owns key krow; element i is query q0 + qb*32 + acc_row(i, h32)
-      f32x16 pm, ds;
+      f32x16& pm = s;   // exponent, then probability (in place)
+      f32x16& ds = dp;  // dP - delta, then dS (in place)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int r4 = qb * 32 + 8 * g + 4 * h32;
@@ -391,16 +402,24 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int i = 4 * g + j;
-          bool vis = true;
-          if (need_mask) {
-            const int ql = r4 + j;
-            if (p.causal) vis = gk <= p.q_offset + q0 + ql;
-            if (segs) vis = vis && (sm.seg[st][ql] == myseg);
-          }
-          const float pr = vis ? fast_exp2(__builtin_fmaf(s[i], p.scale_log2, -l4[j])) : 0.f;
-          pm[i] = pr;
-          ds[i] = pr * (dp[i] - d4[j]);
+          pm[i] = __builtin_fmaf(s[i], p.scale_log2, -l4[j]);
+          ds[i] = dp[i] - d4[j];
         }
+      }
+      // masked scores get exponent -inf (a select, not a branch): exp2(-inf) = 0
+      if (need_mask) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int ql = qb * 32 + acc_row(i, h32);
+          const int32_t qs = segs ? sm.seg[st][ql] : myseg;
+          const bool vis = (!p.causal | (gk <= p.q_offset + q0 + ql)) & (qs == myseg);
+          pm[i] = vis ? pm[i] : -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        pm[i] = fast_exp2(pm[i]);
+        ds[i] *= pm[i];
       }
       const bf16x8 pb[2] = {pack8(pm, 0), pack8(pm, 1)};
       const bf16x8 dsb[2] = {pack8(ds, 0), pack8(ds, 1)};

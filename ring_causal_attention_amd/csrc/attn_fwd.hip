@@ -244,10 +244,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdParams p)
           const int32_t ks = segs ? sm.seg[st][kl] : 0;
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) {
-            bool vis = in_range;
-            if (p.causal) vis = vis && (p.k_offset + key <= gq[qb]);
-            if (segs) vis = vis && (ks == myseg[qb]);
-            if (!vis) s[kb][qb][i] = -INFINITY;
+            const bool vis = in_range & (!p.causal | (p.k_offset + key <= gq[qb])) & (!segs | (ks == myseg[qb]));
+            s[kb][qb][i] = vis ? s[kb][qb][i] : -INFINITY;
           }
         }
     }
