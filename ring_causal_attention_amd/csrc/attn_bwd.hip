@@ -20,6 +20,8 @@
 //  Tiles travel HBM -> LDS by buffer loads that write LDS directly (double-buffered).  Recomputing
 //  S and dP in both kernels costs two extra products over the five the method needs; in exchange
 //  no partial dQ is ever written to or reduced through memory.
+#include <type_traits>
+
 #include "attn_common.hpp"
 #include "profile.hpp"
 
@@ -27,6 +29,18 @@ namespace lwm {
 namespace {
 
 constexpr int kTileBytes = 64 * 256;  // 64 rows x 128 bf16
+
+// Scheduling pattern for the preceding straight-line code: N groups of one MFMA, NV VALU
+// instructions and ND LDS reads, so VALU work is issued while each MFMA runs.
+template <int N, int NV, int ND>
+__device__ __forceinline__ void interleave() {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);  // VALU
+    __builtin_amdgcn_sched_group_barrier(0x100, ND, 0);  // LDS read
+  }
+}
 
 // ------------------------------------------------------------------------------ delta
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
@@ -155,8 +169,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
   for (int db = 0; db < 4; ++db) tr_offsets(lane, db, tlo[db], thi[db]);
 
   if (ntiles > 0) issue(t_begin, 0);
-  for (int it = 0; it < ntiles; ++it) {
-    const int st = it & 1;
+  auto tile = [&](int st, int it) {
     const int k0 = (t_begin + it) * BN;
     wait_vmcnt<0>();
     __syncthreads();
@@ -174,7 +187,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
       active = active && !(ts1 < wseg0 || ts0 > wseg1);
       need_mask = need_mask || !(ts0 == ts1 && wseg0 == wseg1 && ts0 == wseg0);
     }
-    if (!active) continue;
+    if (!active) return;
 
     // S^T = K Q^T and dP^T = V dO^T, one key block at a time; operands read one step ahead
     bf16x8 dsb[2][2];
@@ -231,7 +244,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-  }
+  };
+  for (int it = 0; it < ntiles; ++it) tile(it & 1, it);
   __syncthreads();
   uint8_t* stage_w = reinterpret_cast<uint8_t*>(&sm) + w * (32 * D * 2);
   store_rows_bf16(stage_w, acc, p.scale, p.dq + b * p.sdq.b + hh * p.sdq.h + wr0 * p.sdq.l, p.sdq.l,
@@ -239,21 +253,28 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
 }
 
 // ------------------------------------------------------------------------------ dK / dV
-constexpr int BQ = 64;  // queries per tile in the dK/dV kernel
+// A workgroup owns 128 keys and has 8 waves, two per SIMD: wave w handles the 32 keys
+// k0 + 32 (w % 4) against the query half w / 4 of every 64-query tile, so each wave keeps one
+// 32-key dK^T and dV^T accumulator pair (128 registers) and the SIMD's two waves overlap one's
+// MFMAs with the other's softmax.  The two partial sums of a key block are added through LDS at
+// the end.  The workgroup's K and V tiles sit in LDS for the whole pass.
+constexpr int BQ = 64;   // queries per tile
+constexpr int kDkdvWaves = 8;
 struct SmemDkdv {
-  uint8_t qo[2][2][kTileBytes];  // [stage][Q, dO] row-major swizzled
-  uint8_t kv[2][2 * kTileBytes]; // [K, V] of the workgroup's 128 keys (loaded once), row-major swizzled
+  uint8_t qo[2][2][kTileBytes];   // [stage][Q, dO] row-major swizzled
+  uint8_t kv[2][2 * kTileBytes];  // [K, V] of the workgroup's 128 keys, row-major swizzled
   float lse2[2][BQ];
   float dlt[2][BQ];
   int32_t seg[2][BQ];
 };
-static_assert(sizeof(SmemDkdv) >= kWaves * 32 * D * 2, "epilogue staging must fit");
+static_assert(sizeof(SmemDkdv) >= 4 * 32 * D * 4 * 2, "partial-sum exchange must fit");
 
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
-  constexpr int NW = 32, BK = kWaves * NW;
+__global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams p) {
+  constexpr int BK = 128;
   __shared__ __attribute__((aligned(1024))) SmemDkdv sm;
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c32 = lane & 31, h32 = lane >> 5;
+  const int kb = w & 3, qh = w >> 2;  // key block of 32, query half of each 64-query tile
   const int nkt = (p.Lk + BK - 1) / BK;
   int bh, kt;
   map_block(blockIdx.x, nkt, p.B * p.H, false, bh, kt);
@@ -275,7 +296,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
   const int t_begin = qbeg / BQ;
   const int ntiles = (qend > qbeg) ? (qend + BQ - 1) / BQ - t_begin : 0;
 
-  const int wk0 = k0 + w * NW, wk1 = min(wk0 + NW, p.Lk) - 1;
+  const int wk0 = k0 + kb * 32, wk1 = min(wk0 + 32, p.Lk) - 1;
   const bool wave_keys = wk1 >= wk0;
   int32_t wseg0 = 0, wseg1 = 0;
   if (segs && wave_keys) {
@@ -286,7 +307,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
   const int64_t gk = p.k_offset + krow;
   const int32_t myseg = segs ? p.seg_k[(int64_t)b * p.Lk + min(krow, p.Lk - 1)] : 0;
 
-  // the workgroup's K and V (128 keys each) go to LDS once; each wave reads its 32 keys' operands
+  // the workgroup's K and V (128 rows each) into LDS: 32 blocks of 1 KB per tensor, 4 per wave
   {
     const uint8_t* kgb = reinterpret_cast<const uint8_t*>(p.k + b * p.sk.b + hh * p.sk.h);
     const uint8_t* vgb = reinterpret_cast<const uint8_t*>(p.v + b * p.sv.b + hh * p.sv.h);
@@ -294,16 +315,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kgb + k0 * klb, (int64_t)(p.Lk - 1 - k0) * klb + 256);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vgb + k0 * vlb, (int64_t)(p.Lk - 1 - k0) * vlb + 256);
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {  // 32 blocks of 1 KB per tensor, 8 per wave
-      const int blk = w * 8 + r;
+    for (int r = 0; r < 4; ++r) {
+      const int blk = w * 4 + r;
       const int row = blk * 4 + (lane >> 4);
       const int c = (lane & 15) ^ swz16(row);
       load_lds16(rk, &sm.kv[0][blk * 1024], (int)(row * klb) + c * 16);
       load_lds16(rv, &sm.kv[1][blk * 1024], (int)(row * vlb) + c * 16);
     }
   }
-  const uint8_t* kw = sm.kv[0] + w * 8192;  // this wave's 32 keys
-  const uint8_t* vw = sm.kv[1] + w * 8192;
+  const uint8_t* kw = sm.kv[0] + kb * 8192;  // this wave's 32 keys
+  const uint8_t* vw = sm.kv[1] + kb * 8192;
+
   f32x16 dk[4], dv[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
@@ -317,29 +339,26 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
   const float* lse2_row = p.lse2 + ((int64_t)b * p.H + hh) * p.Lq;
   const float* dlt_row = p.delta + ((int64_t)b * p.H + hh) * p.Lq;
   const int32_t* segq_row = segs ? p.seg_q + (int64_t)b * p.Lq : nullptr;
-  int ld_voff_q[4], ld_voff_o[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int row = (w * 4 + r) * 4 + (lane >> 4);
-    const int c = (lane & 15) ^ swz16(row);
-    ld_voff_q[r] = (int)(row * ql_bytes) + c * 16;
-    ld_voff_o[r] = (int)(row * ol_bytes) + c * 16;
-  }
+  // per q-tile: 16 blocks of 1 KB for Q and 16 for dO, two per wave
+  const int ld_row0 = (w * 2) * 4 + (lane >> 4), ld_row1 = ld_row0 + 4;
+  const int ld_voff_q0 = (int)(ld_row0 * ql_bytes) + (((lane & 15) ^ swz16(ld_row0)) << 4);
+  const int ld_voff_q1 = (int)(ld_row1 * ql_bytes) + (((lane & 15) ^ swz16(ld_row1)) << 4);
+  const int ld_voff_o0 = (int)(ld_row0 * ol_bytes) + (((lane & 15) ^ swz16(ld_row0)) << 4);
+  const int ld_voff_o1 = (int)(ld_row1 * ol_bytes) + (((lane & 15) ^ swz16(ld_row1)) << 4);
   auto issue = [&](int tile, int st) {
     const int q0 = tile * BQ;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(qg + q0 * ql_bytes, q_extent - q0 * ql_bytes);
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(og + q0 * ol_bytes, o_extent - q0 * ol_bytes);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      load_lds16(rq, &sm.qo[st][0][(w * 4 + r) * 1024], ld_voff_q[r]);
-      load_lds16(ro, &sm.qo[st][1][(w * 4 + r) * 1024], ld_voff_o[r]);
-    }
+    load_lds16(rq, &sm.qo[st][0][(w * 2) * 1024], ld_voff_q0);
+    load_lds16(rq, &sm.qo[st][0][(w * 2 + 1) * 1024], ld_voff_q1);
+    load_lds16(ro, &sm.qo[st][1][(w * 2) * 1024], ld_voff_o0);
+    load_lds16(ro, &sm.qo[st][1][(w * 2 + 1) * 1024], ld_voff_o1);
     const int64_t rem = (int64_t)(p.Lq - q0) * 4;
     if (w == 0) load_lds4(make_rsrc(lse2_row + q0, rem), &sm.lse2[st][0], lane * 4);
     if (w == 1) load_lds4(make_rsrc(dlt_row + q0, rem), &sm.dlt[st][0], lane * 4);
     if (segs && w == 2) load_lds4(make_rsrc(segq_row + q0, rem), &sm.seg[st][0], lane * 4);
   };
-  int roff[8];  // Q / dO row-major operand for feature step sd (+8192 for the second query block)
+  int roff[8];  // row-major operand (Q, dO, K, V rows) for feature step sd
 #pragma unroll
   for (int sd = 0; sd < 8; ++sd) roff[sd] = rm_offset(c32, 2 * sd + h32);
   int tlo[4], thi[4];  // Q^T / dO^T operand for feature block db (+4096 per 16-query group)
@@ -353,102 +372,102 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
     wait_vmcnt<0>();
     __syncthreads();
     if (it + 1 < ntiles) issue(t_begin + it + 1, st ^ 1);
-    const uint8_t* qt = sm.qo[st][0];
-    const uint8_t* ot = sm.qo[st][1];
-    bool active = wave_keys;
+    const uint8_t* qt = sm.qo[st][0] + qh * 8192;  // this wave's 32 queries
+    const uint8_t* ot = sm.qo[st][1] + qh * 8192;
+    const int wq0 = q0 + qh * 32;
+    bool active = wave_keys && (wq0 < p.Lq);
     bool need_mask = false;
     if (p.causal) {
-      active = active && (p.q_offset + q0 + BQ - 1 >= p.k_offset + wk0);
-      need_mask = p.k_offset + wk1 > p.q_offset + q0;
+      active = active && (p.q_offset + wq0 + 31 >= p.k_offset + wk0);
+      need_mask = p.k_offset + wk1 > p.q_offset + wq0;
     }
     if (segs) {
-      const int32_t ts0 = sm.seg[st][0], ts1 = sm.seg[st][min(BQ, p.Lq - q0) - 1];
+      const int32_t ts0 = sm.seg[st][qh * 32], ts1 = sm.seg[st][min(qh * 32 + 32, p.Lq - q0) - 1];
       active = active && !(ts1 < wseg0 || ts0 > wseg1);
       need_mask = need_mask || !(ts0 == ts1 && wseg0 == wseg1 && ts0 == wseg0);
     }
     if (!active) continue;
 
+    // S = Q K^T and dP = dO V^T (32 queries x 32 keys)
+    f32x16 s, dp;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys
-      f32x16 s, dp;
+    for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
-      // operands (Q, K, dO, V rows; the same lane layout) read one feature step ahead
-      bf16x8 f[2][4];
-      auto fread = [&](int sd, bf16x8 (&dst)[4]) {
-        dst[0] = as_bf16x8(*reinterpret_cast<const u32x4*>(qt + qb * 8192 + roff[sd]));
-        dst[1] = as_bf16x8(*reinterpret_cast<const u32x4*>(kw + roff[sd]));
-        dst[2] = as_bf16x8(*reinterpret_cast<const u32x4*>(ot + qb * 8192 + roff[sd]));
-        dst[3] = as_bf16x8(*reinterpret_cast<const u32x4*>(vw + roff[sd]));
-      };
-      fread(0, f[0]);
+    for (int sd = 0; sd < 8; ++sd) {
+      s = mfma_32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(qt + roff[sd])),
+                        as_bf16x8(*reinterpret_cast<const u32x4*>(kw + roff[sd])), s);
+      dp = mfma_32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(ot + roff[sd])),
+                         as_bf16x8(*reinterpret_cast<const u32x4*>(vw + roff[sd])), dp);
+    }
+    // lane owns key krow; element i is query wq0 + acc_row(i, h32)
 #pragma unroll
-      for (int sd = 0; sd < 8; ++sd) {
-        if (sd + 1 < 8) fread(sd + 1, f[(sd + 1) & 1]);
-        __builtin_amdgcn_sched_barrier(0);
-        s = mfma_32x32x16(f[sd & 1][0], f[sd & 1][1], s);
-        dp = mfma_32x32x16(f[sd & 1][2], f[sd & 1][3], dp);
-        __builtin_amdgcn_sched_barrier(0);
+    for (int g = 0; g < 4; ++g) {
+      const int r4 = qh * 32 + 8 * g + 4 * h32;
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse2[st][r4]);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dlt[st][r4]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 4 * g + j;
+        s[i] = __builtin_fmaf(s[i], p.scale_log2, -l4[j]);
+        dp[i] = dp[i] - d4[j];
       }
-      // lane owns key krow; element i is query q0 + qb*32 + acc_row(i, h32)
-      f32x16& pm = s;   // exponent, then probability (in place)
-      f32x16& ds = dp;  // dP - delta, then dS (in place)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int r4 = qb * 32 + 8 * g + 4 * h32;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse2[st][r4]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dlt[st][r4]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = 4 * g + j;
-          pm[i] = __builtin_fmaf(s[i], p.scale_log2, -l4[j]);
-          ds[i] = dp[i] - d4[j];
-        }
-      }
+    }
+    if (need_mask) {
       // masked scores get exponent -inf (a select, not a branch): exp2(-inf) = 0
-      if (need_mask) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int ql = qb * 32 + acc_row(i, h32);
-          const int32_t qs = segs ? sm.seg[st][ql] : myseg;
-          const bool vis = (!p.causal | (gk <= p.q_offset + q0 + ql)) & (qs == myseg);
-          pm[i] = vis ? pm[i] : -INFINITY;
-        }
-      }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        pm[i] = fast_exp2(pm[i]);
-        ds[i] *= pm[i];
+        const int ql = qh * 32 + acc_row(i, h32);
+        const int32_t qs = segs ? sm.seg[st][ql] : myseg;
+        const bool vis = (!p.causal | (gk <= p.q_offset + q0 + ql)) & (qs == myseg);
+        s[i] = vis ? s[i] : -INFINITY;
       }
-      const bf16x8 pb[2] = {pack8(pm, 0), pack8(pm, 1)};
-      const bf16x8 dsb[2] = {pack8(ds, 0), pack8(ds, 1)};
-      // dV^T += dO^T P, dK^T += Q^T dS (transposed operands read two ahead)
-      bf16x8 fo_t[3], fq_t[3];
-      auto tread = [&](const uint8_t* tile, int n) {
-        return read_xt(tile + (qb * 2 + (n >> 2)) * 4096, tlo[n & 3], thi[n & 3]);
-      };
-      fo_t[0] = tread(ot, 0);
-      fq_t[0] = tread(qt, 0);
-      fo_t[1] = tread(ot, 1);
-      fq_t[1] = tread(qt, 1);
+    }
 #pragma unroll
-      for (int n = 0; n < 8; ++n) {  // n = 16-query group (within this block) * 4 + feature block
-        if (n + 2 < 8) {
-          fo_t[(n + 2) % 3] = tread(ot, n + 2);
-          fq_t[(n + 2) % 3] = tread(qt, n + 2);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        const int u = n >> 2, db = n & 3;
-        dv[db] = mfma_32x32x16(fo_t[n % 3], pb[u], dv[db]);
-        dk[db] = mfma_32x32x16(fq_t[n % 3], dsb[u], dk[db]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    for (int i = 0; i < 16; ++i) {
+      s[i] = fast_exp2(s[i]);
+      dp[i] *= s[i];
+    }
+    const bf16x8 pb[2] = {pack8(s, 0), pack8(s, 1)};
+    const bf16x8 dsb[2] = {pack8(dp, 0), pack8(dp, 1)};
+    // dV^T += dO^T P, dK^T += Q^T dS (transposed operands by transposing reads)
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {  // n = 16-query group * 4 + feature block
+      const int u = n >> 2, db = n & 3;
+      dv[db] = mfma_32x32x16(read_xt(ot + u * 4096, tlo[db], thi[db]), pb[u], dv[db]);
+      dk[db] = mfma_32x32x16(read_xt(qt + u * 4096, tlo[db], thi[db]), dsb[u], dk[db]);
     }
   }
   __syncthreads();
+  // add the second query half's partial sums (waves 4..7) to the first's (waves 0..3) via LDS
+  f32x4* xch = reinterpret_cast<f32x4*>(&sm);  // [key block][tensor][db][16 groups of 4][64 lanes]
+  if (qh == 1) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        xch[(((kb * 2 + 0) * 4 + db) * 4 + g) * 64 + lane] = f32x4{dk[db][4 * g], dk[db][4 * g + 1], dk[db][4 * g + 2], dk[db][4 * g + 3]};
+        xch[(((kb * 2 + 1) * 4 + db) * 4 + g) * 64 + lane] = f32x4{dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]};
+      }
+  }
+  __syncthreads();
+  if (qh == 0) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 a = xch[(((kb * 2 + 0) * 4 + db) * 4 + g) * 64 + lane];
+        const f32x4 c = xch[(((kb * 2 + 1) * 4 + db) * 4 + g) * 64 + lane];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          dk[db][4 * g + j] += a[j];
+          dv[db][4 * g + j] += c[j];
+        }
+      }
+  }
+  __syncthreads();
+  // waves 0..3 store (store_rows_bf16 has block-wide barriers: every wave takes part)
   uint8_t* stage_w = reinterpret_cast<uint8_t*>(&sm) + w * (32 * D * 2);
-  const int rows_valid = max(0, min(32, p.Lk - wk0));
+  const int rows_valid = qh == 0 ? max(0, min(32, p.Lk - wk0)) : 0;
   store_rows_bf16(stage_w, dk, p.scale, p.dk + b * p.sdk.b + hh * p.sdk.h + wk0 * p.sdk.l, p.sdk.l, rows_valid);
   store_rows_bf16(stage_w, dv, 1.f, p.dv + b * p.sdv.b + hh * p.sdv.h + wk0 * p.sdv.l, p.sdv.l, rows_valid);
 }
@@ -465,7 +484,7 @@ hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t stream) {
   }
   if (p.Lk > 0) {
     const int nkt = (p.Lk + 127) / 128;
-    LWM_LAUNCH("bwd_dkdv", bwd_dkdv_kernel, dim3(nkt * p.B * p.H), dim3(kThreads), stream, p);
+    LWM_LAUNCH("bwd_dkdv", bwd_dkdv_kernel, dim3(nkt * p.B * p.H), dim3(kDkdvWaves * kWave), stream, p);
   }
   return hipGetLastError();
 }

@@ -181,8 +181,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdParams p)
 
   if (ntiles > 0) issue(t_begin, 0);
 
-  for (int it = 0; it < ntiles; ++it) {
-    const int st = it & 1;
+  auto tile = [&](int st, int it) {
     const int k0 = (t_begin + it) * BN;
     wait_vmcnt<0>();   // this wave's loads of tile `it` have landed in LDS
     __syncthreads();   // ... and every other wave's; everyone is done with tile it-1
@@ -202,7 +201,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdParams p)
       active = active && !(ts1 < wseg0 || ts0 > wseg1);
       need_mask = need_mask || !(ts0 == ts1 && wseg0 == wseg1 && ts0 == wseg0);
     }
-    if (!active) continue;
+    if (!active) return;
 
     // ---- S^T = K Q^T: [2 key blocks][QB query blocks] of 32x32.  K fragments are read two
     // feature steps ahead of the MFMAs that consume them (scheduling barriers keep the order).
@@ -319,7 +318,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdParams p)
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-  }
+  };
+  for (int it = 0; it < ntiles; ++it) tile(it & 1, it);
   __syncthreads();  // all waves are done reading tiles before the epilogue reuses the LDS
 
   // ---- epilogue: O = acc / l, lse = (m + log2 l) ln 2
