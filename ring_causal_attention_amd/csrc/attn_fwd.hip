@@ -254,12 +254,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdParams p)
     bool need_rescale = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float v = -INFINITY;
+      // balanced tree over the 32 in-lane scores (short dependency chains), then the lane pair
+      float t[8];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) v = fmaxf(v, s[kb][qb][i]);
-      v = fmaxf(v, swap_halves(v));
+      for (int c = 0; c < 8; ++c) {
+        const f32x16& a = s[c >> 2][qb];
+        const int o = (c & 3) * 4;
+        t[c] = fmaxf(fmaxf(a[o], a[o + 1]), fmaxf(a[o + 2], a[o + 3]));
+      }
+      const float v = pair_max(fmaxf(fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])), fmaxf(fmaxf(t[4], t[5]), fmaxf(t[6], t[7]))));
       mx[qb] = v * p.scale_log2;
       need_rescale = need_rescale || (mx[qb] > m[qb] + kRescaleSlack);
     }
@@ -282,7 +285,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdParams p)
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const float moff = (m[qb] == -INFINITY) ? 0.f : m[qb];
-      float lsum = 0.f;
+      float lsum[4] = {0.f, 0.f, 0.f, 0.f};  // independent partial sums (short chains)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -293,12 +296,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdParams p)
             const float e0 = fast_exp2(__builtin_fmaf(s[kb][qb][u * 8 + 2 * j], p.scale_log2, -moff));
             const float e1 = fast_exp2(__builtin_fmaf(s[kb][qb][u * 8 + 2 * j + 1], p.scale_log2, -moff));
             const uint32_t word = pack_bf16x2(e0, e1);
-            lsum = sum_bf16x2(word, lsum);
+            lsum[j] = sum_bf16x2(word, lsum[j]);
             packed[j] = word;
           }
           pb[kb][u][qb] = as_bf16x8(packed);
         }
-      l[qb] += lsum;
+      l[qb] += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
     }
 
     // ---- O^T += V^T P^T (V^T operands by transposing reads of the row-major V tile, issued
@@ -329,7 +332,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdParams p)
   for (int qb = 0; qb < QB; ++qb) {
     const int r0 = wr0 + qb * 32;
     const int rows_valid = max(0, min(32, p.Lq - r0));
-    const float lt = l[qb] + swap_halves(l[qb]);
+    const float lt = pair_sum(l[qb]);
     const bool any = (lt > 0.f) && (m[qb] != -INFINITY);
     const float inv = any ? 1.f / lt : 0.f;
     const float lse = any ? (m[qb] + log2f(lt)) * kLn2 : -INFINITY;

@@ -13,6 +13,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -62,6 +63,18 @@ __device__ __forceinline__ constexpr int acc_row(int i, int h) { return 8 * (i >
 // Value held by lane (l ^ 32).
 __device__ __forceinline__ float swap_halves(float x) {
   return __shfl_xor(x, 32, kWave);
+}
+
+// max / sum of x over the lane pair (l, l ^ 32), in every lane.  v_permlane32_swap exchanges the
+// two 32-lane halves between its two operands, so combining the two results pairs each lane with
+// its partner, whichever half each operand ends up holding; no LDS round trip.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Integer min / max for 64-bit values (the generic overloads may go through double).
