@@ -7,24 +7,30 @@
 // RingAttention撬动百万Token多模态世界", section 3.1).
 //
 // Design (bf16 path):
-//  * A workgroup of 4 waves owns BM = 4 * 32 * QB query rows of one (batch, head); each wave owns
-//    32 * QB rows whose Q fragments stay in registers for the whole pass.
-//  * K and V tiles of 64 keys stream HBM -> registers -> LDS, double-buffered: the global loads of
-//    tile j+1 are in flight while tile j is computed.  K is stored row-major with a 16-byte-chunk
-//    XOR swizzle; V is stored transposed (feature-major) with the keys of each 16-key group
-//    permuted to match the MFMA accumulator layout, so P never leaves registers.
-//  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: each lane then
-//    holds one query column, so the row max / row sum are in-lane plus a single exchange between
-//    the two wave halves, and the O^T accumulator's rescale is a per-lane multiply.
-//  * P^T (rounded to bf16) is the B operand of O^T += V^T P^T straight from the accumulator
-//    registers.  l sums the bf16-rounded p (v_dot2_f32_bf16), so O is a true convex combination.
-//  * The running max is only raised when a row's new max exceeds it by more than 2^8 (log2
-//    domain); in between p <= 256, which is exact in fp32 and keeps rescales rare.
-//  * Tiles wholly outside the causal / segment range are never visited; the mask is evaluated
-//    only on tiles that straddle a boundary or the ragged end.
+//  * A workgroup of 4 waves owns 128 query rows of one (batch, head); each wave owns 32 rows whose
+//    Q fragments stay in registers for the whole pass.  Two workgroups share a CU.
+//  * K and V tiles of 64 keys go HBM -> LDS with buffer loads that write LDS directly (rows past
+//    the end read as zero), row-major with a 16-byte-chunk XOR swizzle chosen by the address each
+//    lane loads from.  K runs one tile ahead of V; each has its own double buffer.
+//  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: each lane holds
+//    one query column, so the row max / row sum are in-lane plus one exchange between the two
+//    wave halves (v_permlane32_swap), and the O^T rescale is a per-lane multiply.
+//  * Software pipeline: the 16 MFMAs of S_(j+1) are interleaved with the softmax of tile j, one
+//    slice of vector work behind each MFMA, so a wave keeps its matrix core busy while it does
+//    the exponentials; then O^T += V_j^T P_j^T with V^T operands from transposing LDS reads
+//    (ds_read_b64_tr_b16) and P^T (bf16) straight from registers.
+//  * l sums the bf16-rounded p, so O is a true convex combination.  The running max is only
+//    raised when a row's new max exceeds it by more than 2^8 (log2 domain); in between p <= 256,
+//    exact in fp32, and rescales stay rare.
+//  * Key tiles outside the workgroup's causal / segment range are never visited.  Inside it, a
+//    tile is masked element-wise only when it straddles a boundary or the ragged end (a tile one
+//    wave sees nothing of is computed fully masked: there are few, and the pipeline stays
+//    branch-free).
 //  * Workgroups are numbered longest-first, and when B*H is a multiple of 8 the (batch, head)
 //    pairs are dealt to the 8 XCDs so the query tiles sharing one head's K/V run on one L2.
 #include <float.h>
+
+#include <type_traits>
 
 #include "attn_common.hpp"
 #include "profile.hpp"
@@ -35,14 +41,6 @@ namespace {
 constexpr int BN = 64;                 // keys per tile (bf16 path)
 constexpr int kTileBytes = BN * 256;   // one K or V tile: 64 rows x 128 bf16
 constexpr float kRescaleSlack = 8.0f;  // log2 units: p <= 2^8 between rescales
-
-// Two stages of (K tile, V tile, 64 segment ids); 2 workgroups fit in one CU's LDS.
-struct SmemBf16 {
-  uint8_t kv[2][2][kTileBytes];
-  int32_t seg[2][BN];
-};
-static_assert(sizeof(SmemBf16) <= 80 * 1024, "two workgroups per CU must fit in LDS");
-static_assert(sizeof(SmemBf16) >= kWaves * 32 * D * 4, "epilogue staging must fit");
 
 // Key range [kbeg, kend) that can be visible to query rows [r0, r1] (inclusive).
 __device__ inline void key_range(const FwdParams& p, int b, int r0, int r1, int& kbeg, int& kend) {
@@ -62,14 +60,26 @@ __device__ inline void key_range(const FwdParams& p, int b, int r0, int r1, int&
 }
 
 // ---------------------------------------------------------------------------- bf16 kernel
-// Streams K/V tiles HBM -> LDS with buffer loads that write LDS directly (no staging registers,
-// no per-tile address arithmetic beyond a scalar tile base; rows past the end read as zero).
-// The swizzle of a tile is chosen by the source address each lane loads.
-template <int QB>
+// Software-pipelined over key tiles: while the MFMAs of S_(j+1) = K_(j+1) Q^T run, the same wave
+// issues the softmax of tile j (independent VALU work), so the matrix cores and the vector ALUs
+// of a SIMD work at the same time even within one wave; O += V_j^T P_j follows.  K runs one tile
+// ahead of V, so K tiles and V tiles (with their segment ids) are double-buffered separately.
+struct SmemSp {
+  union {
+    struct {
+      uint8_t k[2][kTileBytes];
+      uint8_t v[2][kTileBytes];
+      int32_t seg[2][BN];
+    } t;
+    uint8_t stage_rows[kWaves][32 * D * 4];  // epilogue staging (fp32 rows), after the loop
+  };
+};
+static_assert(sizeof(SmemSp) <= 80 * 1024, "two workgroups per CU must fit in LDS");
+
+template <bool kSegs, bool kRing>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdParams p) {
-  constexpr int MW = 32 * QB;
-  constexpr int BM = kWaves * MW;
-  __shared__ __attribute__((aligned(1024))) SmemBf16 sm;
+  constexpr int BM = kWaves * 32;
+  __shared__ __attribute__((aligned(1024))) SmemSp sm;
 
   // the wave index is uniform; say so, so LDS bases derived from it stay in scalar registers
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -86,12 +96,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdParams p)
   const int t_begin = kbeg / BN;
   const int ntiles = (kend > kbeg) ? (kend + BN - 1) / BN - t_begin : 0;
 
-  const int wr0 = q0 + w * MW;
-  const int wr1 = min(wr0 + MW, p.Lq) - 1;  // may be < wr0 for a ragged last tile
+  const int wr0 = q0 + w * 32;
+  const int wr1 = min(wr0 + 32, p.Lq) - 1;  // may be < wr0 for a ragged last tile
   const bool wave_rows = wr1 >= wr0;
-  const bool segs = p.seg_q != nullptr;
   int32_t wseg0 = 0, wseg1 = 0;
-  if (segs && wave_rows) {
+  if (kSegs && wave_rows) {
     wseg0 = p.seg_q[(int64_t)b * p.Lq + wr0];
     wseg1 = p.seg_q[(int64_t)b * p.Lq + wr1];
   }
@@ -101,261 +110,273 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdParams p)
   const uint8_t* vg = reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(p.v) + b * p.sv.b + hh * p.sv.h);
   const int64_t kl_bytes = p.sk.l * 2, vl_bytes = p.sv.l * 2;
   const int64_t k_extent = (int64_t)(p.Lk - 1) * kl_bytes + 256, v_extent = (int64_t)(p.Lk - 1) * vl_bytes + 256;
-  const int32_t* segk_row = segs ? p.seg_k + (int64_t)b * p.Lk : nullptr;
+  const int32_t* segk_row = kSegs ? p.seg_k + (int64_t)b * p.Lk : nullptr;
 
-  int qrow[QB];
-  int64_t gq[QB];
-  int32_t myseg[QB];
-  bf16x8 qreg[QB][8];
+  const int qrow = wr0 + c32;
+  const int64_t gq = p.q_offset + qrow;
+  const int32_t myseg = kSegs ? p.seg_q[(int64_t)b * p.Lq + min(qrow, p.Lq - 1)] : 0;
+  bf16x8 qreg[8];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    qrow[qb] = wr0 + qb * 32 + c32;
-    gq[qb] = p.q_offset + qrow[qb];
-    myseg[qb] = segs ? p.seg_q[(int64_t)b * p.Lq + min(qrow[qb], p.Lq - 1)] : 0;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (qrow[qb] < p.Lq) v = *reinterpret_cast<const u32x4*>(qg + qrow[qb] * p.sq.l + s * 16 + h32 * 8);
-      qreg[qb][s] = as_bf16x8(v);
-    }
+  for (int s = 0; s < 8; ++s) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (qrow < p.Lq) v = *reinterpret_cast<const u32x4*>(qg + qrow * p.sq.l + s * 16 + h32 * 8);
+    qreg[s] = as_bf16x8(v);
   }
 
   // running state: O^T accumulators, row max m (log2-scaled), partial row sum l (this half's keys)
-  f32x16 acc[QB][4];
-  float m[QB], l[QB], m_init[QB];
-  const bool ring = p.mode == 1;
+  f32x16 acc[4];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[qb][db][i] = 0.f;
-    m[qb] = -INFINITY;
-    l[qb] = 0.f;
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  uint8_t* stage_w = sm.stage_rows[w];
+  if (kRing && ntiles > 0) {
+    load_rows_f32(stage_w, acc, p.o_acc + b * p.soa.b + hh * p.soa.h + wr0 * p.soa.l, p.soa.l,
+                  max(0, min(32, p.Lq - wr0)));
+    const float ls = qrow < p.Lq ? p.lse_acc[((int64_t)b * p.H + hh) * p.Lq + qrow] : -INFINITY;
+    m = ls * kLog2e;
+    l = h32 == 0 ? 1.f : 0.f;
   }
-  uint8_t* stage_w = reinterpret_cast<uint8_t*>(&sm) + w * (32 * D * 4);
-  if (ring && ntiles > 0) {
-    float* oag = p.o_acc + b * p.soa.b + hh * p.soa.h;
-    const float* lag = p.lse_acc + ((int64_t)b * p.H + hh) * p.Lq;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int r0 = wr0 + qb * 32;
-      load_rows_f32(stage_w, acc[qb], oag + r0 * p.soa.l, p.soa.l, max(0, min(32, p.Lq - r0)));
-      const float ls = qrow[qb] < p.Lq ? lag[qrow[qb]] : -INFINITY;
-      m[qb] = ls * kLog2e;
-      l[qb] = h32 == 0 ? 1.f : 0.f;
-    }
-  }
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) m_init[qb] = m[qb];
+  const float m_init = m;
 
-  // ---- per-lane load plan: wave w fills 1 KB blocks w*4 .. w*4+3 of each tile (4 rows per block);
-  // lane l of a block holds row 4*blk + l/16, physical chunk l%16 = logical chunk ^ swz16(row).
-  int ld_voff_k[4], ld_voff_v[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
+  // ---- loads: wave w fills 1 KB blocks w*4 .. w*4+3 of a tile (4 rows per block); lane l of a
+  // block holds row 4*blk + l/16, physical chunk l%16 = logical chunk ^ swz16(row).
+  auto ld_off = [&](int r, int64_t row_bytes) {
     const int row = (w * 4 + r) * 4 + (lane >> 4);
-    const int c = (lane & 15) ^ swz16(row);
-    ld_voff_k[r] = (int)(row * kl_bytes) + c * 16;
-    ld_voff_v[r] = (int)(row * vl_bytes) + c * 16;
-  }
-  auto issue = [&](int tile, int st) {
-    const int k0 = tile * BN;
+    return (int)(row * row_bytes) + (((lane & 15) ^ swz16(row)) << 4);
+  };
+  auto issue_k = [&](int j) {  // K tile j -> k[j & 1]
+    const int k0 = (t_begin + j) * BN;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + k0 * kl_bytes, k_extent - k0 * kl_bytes);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) load_lds16(rk, &sm.t.k[j & 1][(w * 4 + r) * 1024], ld_off(r, kl_bytes));
+  };
+  auto issue_v = [&](int j) {  // V tile j and its segment ids -> v[j & 1], seg[j & 1]
+    const int k0 = (t_begin + j) * BN;
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + k0 * vl_bytes, v_extent - k0 * vl_bytes);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      load_lds16(rk, &sm.kv[st][0][(w * 4 + r) * 1024], ld_voff_k[r]);
-      load_lds16(rv, &sm.kv[st][1][(w * 4 + r) * 1024], ld_voff_v[r]);
-    }
-    if (segs && w == 0) load_lds4(make_rsrc(segk_row + k0, (int64_t)(p.Lk - k0) * 4), &sm.seg[st][0], lane * 4);
+    for (int r = 0; r < 4; ++r) load_lds16(rv, &sm.t.v[j & 1][(w * 4 + r) * 1024], ld_off(r, vl_bytes));
+    if (kSegs && w == 0) load_lds4(make_rsrc(segk_row + k0, (int64_t)(p.Lk - k0) * 4), &sm.t.seg[j & 1][0], lane * 4);
   };
 
-  // ---- per-lane LDS read offsets (constant over tiles)
-  int koff[8];  // K operand for feature step sd: row c32 (+32 per key block), chunk 2*sd + h32
+  // ---- LDS operand offsets.  K row c32, chunk 2*sd + h32: the XOR swizzle leaves bit 0 of an
+  // even chunk index alone, so the offset is a per-lane base plus ((2*sd) ^ swizzle) * 16.  The
+  // V^T offsets of feature block db differ from block 0's by an XOR of db into chunk bits 2..3.
+  const int kswz = swz16(c32 & 15);
+  const int krow_base = c32 * 256 + (((h32 ^ kswz) & 1) << 4);
+  int koff[8];
 #pragma unroll
-  for (int sd = 0; sd < 8; ++sd) koff[sd] = rm_offset(c32, 2 * sd + h32);
-  int vlo[4], vhi[4];  // V^T operand for feature block db (+4096 per 16-key group)
-#pragma unroll
-  for (int db = 0; db < 4; ++db) tr_offsets(lane, db, vlo[db], vhi[db]);
+  for (int sd = 0; sd < 8; ++sd) koff[sd] = krow_base + (((2 * sd) ^ (kswz & 14)) << 4);
+  int vlo0, vhi0;
+  tr_offsets(lane, 0, vlo0, vhi0);
 
-  if (ntiles > 0) issue(t_begin, 0);
-
-  auto tile = [&](int st, int it) {
-    const int k0 = (t_begin + it) * BN;
-    wait_vmcnt<0>();   // this wave's loads of tile `it` have landed in LDS
-    __syncthreads();   // ... and every other wave's; everyone is done with tile it-1
-    if (it + 1 < ntiles) issue(t_begin + it + 1, st ^ 1);
-    const uint8_t* kt = sm.kv[st][0];
-    const uint8_t* vt = sm.kv[st][1];
-
-    // does this wave see any key of the tile, and does it need the element mask?
-    bool active = wave_rows;
-    bool need_mask = (k0 + BN > p.Lk) || (k0 < kbeg) || (k0 + BN > kend);
-    if (p.causal) {
-      active = active && (p.k_offset + k0 <= p.q_offset + wr1);
-      need_mask = need_mask || (p.k_offset + k0 + BN - 1 > p.q_offset + wr0);
-    }
-    if (segs) {
-      const int32_t ts0 = sm.seg[st][0], ts1 = sm.seg[st][min(BN, p.Lk - k0) - 1];
-      active = active && !(ts1 < wseg0 || ts0 > wseg1);
-      need_mask = need_mask || !(ts0 == ts1 && wseg0 == wseg1 && ts0 == wseg0);
-    }
-    if (!active) return;
-
-    // ---- S^T = K Q^T: [2 key blocks][QB query blocks] of 32x32.  K fragments are read two
-    // feature steps ahead of the MFMAs that consume them (scheduling barriers keep the order).
-    f32x16 s[2][QB];
+  auto kread = [&](const uint8_t* kt, int q) __attribute__((always_inline)) {  // fragment of MFMA q = 2*sd + kb
+    return as_bf16x8(*reinterpret_cast<const u32x4*>(kt + (q & 1) * 8192 + koff[q >> 1]));
+  };
+  // S_j^T = K_j Q^T into s, alone (pipeline prologue)
+  auto mma_s = [&](int j, f32x16 (&s)[2]) __attribute__((always_inline)) {
+    const uint8_t* kt = sm.t.k[j & 1];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
+      for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[kb][qb][i] = 0.f;
-    {
-      bf16x8 kf[3][2];
-      auto kread = [&](int sd, bf16x8 (&dst)[2]) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) dst[kb] = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + kb * 8192 + koff[sd]));
-      };
-      kread(0, kf[0]);
-      kread(1, kf[1]);
-#pragma unroll
-      for (int sd = 0; sd < 8; ++sd) {
-        if (sd + 2 < 8) kread(sd + 2, kf[(sd + 2) % 3]);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma_32x32x16(kf[sd % 3][kb], qreg[qb][sd], s[kb][qb]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
+    for (int q = 0; q < 16; ++q) s[q & 1] = mfma_32x32x16(kread(kt, q), qreg[q >> 1], s[q & 1]);
+  };
 
-    if (need_mask) {
+  // Does tile j need the element mask (ragged end, range edges, causal diagonal, segment edges)?
+  auto need_mask = [&](int j) __attribute__((always_inline)) {
+    const int k0 = (t_begin + j) * BN;
+    bool nm = (k0 + BN > p.Lk) || (k0 < kbeg) || (k0 + BN > kend) || !wave_rows;
+    if (p.causal) nm = nm || (p.k_offset + k0 + BN - 1 > p.q_offset + wr0);
+    if (kSegs) {
+      const int32_t ts0 = sm.t.seg[j & 1][0], ts1 = sm.t.seg[j & 1][min(BN, p.Lk - k0) - 1];
+      nm = nm || !(ts0 == ts1 && wseg0 == wseg1 && ts0 == wseg0);
+    }
+    return nm;
+  };
+  // Element i of key block kb holds tile key kl = kb*32 + 8*(i/4) + 4*h32 + i%4; it is visible iff
+  // kl < lim (ragged end, range end, causal limit) and its segment matches this lane's query.
+  auto apply_mask = [&](int j, f32x16 (&s)[2]) __attribute__((always_inline)) {
+    const int k0 = (t_begin + j) * BN;
+    int64_t lim64 = (int64_t)min(p.Lk, kend) - k0;
+    if (p.causal) lim64 = imin64(lim64, gq - p.k_offset - k0 + 1);
+    const int lim = wave_rows ? (int)imax64(imin64(lim64, BN), 0) - 4 * h32 : -BN;
+    const int32_t* segt = &sm.t.seg[j & 1][4 * h32];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        i32x4 ks = {0, 0, 0, 0};
+        if (kSegs) ks = *reinterpret_cast<const i32x4*>(segt + kb * 32 + 8 * g);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool vis = (kb * 32 + 8 * g + r < lim) & (!kSegs | (ks[r] == myseg));
+          s[kb][4 * g + r] = vis ? s[kb][4 * g + r] : -INFINITY;
+        }
+      }
+  };
+
+  // Online softmax of tile j in 16 slices, so that one slice of vector work can be issued behind
+  // each MFMA of the next tile's scores.  Branch-free: the running max is raised (lazily, by more
+  // than the slack) only when some row of the wave needs it, and alpha, the factor the accumulator
+  // must be scaled by, is exactly 1 otherwise.  Leaves P_j^T (bf16) in pb.
+  bf16x8 pb[2][2];
+  struct SoftmaxState {
+    float t4[4];
+    float alpha, moff;
+    float lsum[4];
+    u32x4 packed[2][2];
+  };
+  auto softmax_slice = [&](int q, const f32x16 (&s)[2], SoftmaxState& x) __attribute__((always_inline)) {
+    if (q < 4) {  // maximum of 8 of the 32 in-lane scores (three-input maxima)
+      const f32x16& a = s[q >> 1];
+      const int o = (q & 1) * 8;
+      float t = fmaxf(fmaxf(a[o], a[o + 1]), a[o + 2]);
+      t = fmaxf(fmaxf(t, a[o + 3]), a[o + 4]);
+      t = fmaxf(fmaxf(t, a[o + 5]), a[o + 6]);
+      x.t4[q] = fmaxf(t, a[o + 7]);
+    } else if (q == 4) {  // row max over the lane pair, lazy raise of the running max
+      const float mx = pair_max(fmaxf(fmaxf(fmaxf(x.t4[0], x.t4[1]), x.t4[2]), x.t4[3])) * p.scale_log2;
+      const bool raise = __any(mx > m + kRescaleSlack);
+      const float mnew = raise ? fmaxf(m, mx) : m;
+      x.alpha = (!raise || mnew == -INFINITY) ? 1.f : fast_exp2(m - mnew);
+      m = mnew;
+      x.moff = (mnew == -INFINITY) ? 0.f : mnew;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) x.lsum[jj] = 0.f;
+    } else if (q < 13) {  // p = exp2(s * scale_log2 - m) for 4 scores, rounded to bf16 pairs
+      const int e = q - 5;  // 0..7: block kb = e / 4, 8-element half u = (e / 2) % 2, word pair (e % 2) * 2
+      const int kb = e >> 2, u = (e >> 1) & 1;
+#pragma unroll
+      for (int jj = (e & 1) * 2; jj < (e & 1) * 2 + 2; ++jj) {
+        const float e0 = fast_exp2(__builtin_fmaf(s[kb][u * 8 + 2 * jj], p.scale_log2, -x.moff));
+        const float e1 = fast_exp2(__builtin_fmaf(s[kb][u * 8 + 2 * jj + 1], p.scale_log2, -x.moff));
+        const uint32_t word = pack_bf16x2(e0, e1);
+        x.lsum[jj] = sum_bf16x2(word, x.lsum[jj]);
+        x.packed[kb][u][jj] = word;
+        // keep the work in this slice: without a use here the compiler sinks it past the MFMAs
+        asm volatile("" ::"v"(word), "v"(x.lsum[jj]));
+      }
+    } else if (q == 13) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kl = kb * 32 + acc_row(i, h32);
-          const int key = k0 + kl;
-          const bool in_range = key < p.Lk;
-          const int32_t ks = segs ? sm.seg[st][kl] : 0;
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            const bool vis = in_range & (!p.causal | (p.k_offset + key <= gq[qb])) & (!segs | (ks == myseg[qb]));
-            s[kb][qb][i] = vis ? s[kb][qb][i] : -INFINITY;
-          }
-        }
-    }
-
-    // ---- online softmax (log2 domain), lazily rescaled
-    float mx[QB];
-    bool need_rescale = false;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      // balanced tree over the 32 in-lane scores (short dependency chains), then the lane pair
-      float t[8];
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const f32x16& a = s[c >> 2][qb];
-        const int o = (c & 3) * 4;
-        t[c] = fmaxf(fmaxf(a[o], a[o + 1]), fmaxf(a[o + 2], a[o + 3]));
-      }
-      const float v = pair_max(fmaxf(fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])), fmaxf(fmaxf(t[4], t[5]), fmaxf(t[6], t[7]))));
-      mx[qb] = v * p.scale_log2;
-      need_rescale = need_rescale || (mx[qb] > m[qb] + kRescaleSlack);
-    }
-    if (__any(need_rescale)) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const float mnew = fmaxf(m[qb], mx[qb]);
-        const float alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(m[qb] - mnew);
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[qb][db][i] *= alpha;
-        l[qb] *= alpha;
-        m[qb] = mnew;
-      }
-    }
-
-    // p = exp2(s * scale_log2 - m), rounded to bf16; l += sum of the rounded values
-    bf16x8 pb[2][2][QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float moff = (m[qb] == -INFINITY) ? 0.f : m[qb];
-      float lsum[4] = {0.f, 0.f, 0.f, 0.f};  // independent partial sums (short chains)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          u32x4 packed;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float e0 = fast_exp2(__builtin_fmaf(s[kb][qb][u * 8 + 2 * j], p.scale_log2, -moff));
-            const float e1 = fast_exp2(__builtin_fmaf(s[kb][qb][u * 8 + 2 * j + 1], p.scale_log2, -moff));
-            const uint32_t word = pack_bf16x2(e0, e1);
-            lsum[j] = sum_bf16x2(word, lsum[j]);
-            packed[j] = word;
-          }
-          pb[kb][u][qb] = as_bf16x8(packed);
-        }
-      l[qb] += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
-    }
-
-    // ---- O^T += V^T P^T (V^T operands by transposing reads of the row-major V tile, issued
-    // two operands ahead of their MFMAs)
-    {
-      bf16x8 vf[3];
-      auto vread = [&](int n) { return read_xt(vt + (n >> 2) * 4096, vlo[n & 3], vhi[n & 3]); };
-      vf[0] = vread(0);
-      vf[1] = vread(1);
-#pragma unroll
-      for (int n = 0; n < 16; ++n) {  // n = 16-key group * 4 + feature block
-        if (n + 2 < 16) vf[(n + 2) % 3] = vread(n + 2);
-        __builtin_amdgcn_sched_barrier(0);
-        const int g = n >> 2, db = n & 3;
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma_32x32x16(vf[n % 3], pb[g >> 1][g & 1][qb], acc[qb][db]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+        for (int u = 0; u < 2; ++u) pb[kb][u] = as_bf16x8(x.packed[kb][u]);
+      l = __builtin_fmaf(l, x.alpha, (x.lsum[0] + x.lsum[1]) + (x.lsum[2] + x.lsum[3]));
     }
   };
-  for (int it = 0; it < ntiles; ++it) tile(it & 1, it);
-  __syncthreads();  // all waves are done reading tiles before the epilogue reuses the LDS
-
-  // ---- epilogue: O = acc / l, lse = (m + log2 l) ln 2
-  uint16_t* og = static_cast<uint16_t*>(p.o);
-  float* lse_row = p.lse ? p.lse + ((int64_t)b * p.H + hh) * p.Lq : nullptr;
+  auto rescale = [&](float alpha) __attribute__((always_inline)) {
+    if (__any(alpha != 1.f)) {
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int r0 = wr0 + qb * 32;
-    const int rows_valid = max(0, min(32, p.Lq - r0));
-    const float lt = pair_sum(l[qb]);
-    const bool any = (lt > 0.f) && (m[qb] != -INFINITY);
-    const float inv = any ? 1.f / lt : 0.f;
-    const float lse = any ? (m[qb] + log2f(lt)) * kLn2 : -INFINITY;
-    if (!ring) {
-      if (og) store_rows_bf16(stage_w, acc[qb], inv, og + b * p.so.b + hh * p.so.h + r0 * p.so.l, p.so.l, rows_valid);
-      if (lse_row && h32 == 0 && qrow[qb] < p.Lq) lse_row[qrow[qb]] = lse;
-    } else {
-      float* lag = p.lse_acc + ((int64_t)b * p.H + hh) * p.Lq;
-      float* oag = p.o_acc + b * p.soa.b + hh * p.soa.h + r0 * p.soa.l;
-      uint16_t* ofg = og ? og + b * p.so.b + hh * p.so.h + r0 * p.so.l : nullptr;
-      if (ntiles > 0) {
-        // a row that saw nothing new keeps its state bit for bit
-        const bool untouched = (m[qb] == m_init[qb]) && (lt == 1.f);
-        const float sc = untouched ? 1.f : inv;
-        store_rows_f32(stage_w, acc[qb], sc, oag, p.soa.l, rows_valid);
-        if (h32 == 0 && qrow[qb] < p.Lq && !untouched) lag[qrow[qb]] = lse;
-        if (ofg) store_rows_bf16(stage_w, acc[qb], sc, ofg, p.so.l, rows_valid);
-      } else if (ofg) {
-        // nothing visible in this shard for the whole tile: the bf16 copy is the state itself
-        f32x16 tmp[4];
-        load_rows_f32(stage_w, tmp, oag, p.soa.l, rows_valid);
-        store_rows_bf16(stage_w, tmp, 1.f, ofg, p.so.l, rows_valid);
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+    }
+  };
+  // O^T += V_j^T P_j^T (V^T operands by transposing reads, issued two MFMAs ahead)
+  auto mma_pv = [&](int j) __attribute__((always_inline)) {
+    const uint8_t* vt = sm.t.v[j & 1];
+    bf16x8 vf[3];
+    auto vread = [&](int n) { return read_xt(vt + (n >> 2) * 4096, vlo0 ^ ((n & 3) << 6), vhi0 ^ ((n & 3) << 6)); };
+    vf[0] = vread(0);
+    vf[1] = vread(1);
+#pragma unroll
+    for (int n = 0; n < 16; ++n) {  // n = 16-key group * 4 + feature block
+      if (n + 2 < 16) vf[(n + 2) % 3] = vread(n + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      const int g = n >> 2, db = n & 3;
+      acc[db] = mfma_32x32x16(vf[n % 3], pb[g >> 1][g & 1], acc[db]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // One step of the pipeline.  On entry s_cur = S_j (raw), K_(j+1) and V_j are in LDS.  Loads of
+  // K_(j+2) and V_(j+1) go into the buffers of K_j and V_(j-1), whose last readers finished before
+  // the previous step's barrier, and are waited for at the end of the step.
+  auto step = [&](int j, f32x16 (&s_cur)[2], f32x16 (&s_next)[2], auto has_next) __attribute__((always_inline)) {
+    constexpr bool kNext = decltype(has_next)::value;
+    if (j + 2 < ntiles) issue_k(j + 2);
+    if (j + 1 < ntiles) issue_v(j + 1);
+    if (need_mask(j)) apply_mask(j, s_cur);
+    SoftmaxState x;
+    if constexpr (kNext) {
+      // MFMA q of S_(j+1) (K fragments four MFMAs ahead), then softmax slice q of tile j
+      const uint8_t* kt = sm.t.k[(j + 1) & 1];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s_next[kb][i] = 0.f;
+      constexpr int kAhead = 3;  // K fragments read this many MFMAs ahead
+      bf16x8 kf[kAhead + 1];
+#pragma unroll
+      for (int q = 0; q < kAhead; ++q) kf[q] = kread(kt, q);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        if (q + kAhead < 16) kf[(q + kAhead) % (kAhead + 1)] = kread(kt, q + kAhead);
+        s_next[q & 1] = mfma_32x32x16(kf[q % (kAhead + 1)], qreg[q >> 1], s_next[q & 1]);
+        softmax_slice(q, s_cur, x);
+        __builtin_amdgcn_sched_barrier(0);
       }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) softmax_slice(q, s_cur, x);
+    }
+    rescale(x.alpha);
+    mma_pv(j);
+    wait_vmcnt<0>();
+    __syncthreads();
+  };
+
+  if (ntiles > 0) {
+    f32x16 s0[2], s1[2];
+    issue_k(0);
+    issue_v(0);
+    if (ntiles > 1) issue_k(1);
+    wait_vmcnt<0>();
+    __syncthreads();
+    mma_s(0, s0);
+    __syncthreads();  // K_0 is read by every wave before step 0 reloads its buffer
+    int j = 0;
+    for (; j + 2 < ntiles; j += 2) {
+      step(j, s0, s1, std::true_type{});
+      step(j + 1, s1, s0, std::true_type{});
+    }
+    if (j + 1 < ntiles) {
+      step(j, s0, s1, std::true_type{});
+      step(j + 1, s1, s0, std::false_type{});
+    } else {
+      step(j, s0, s1, std::false_type{});
+    }
+  }
+
+  // ---- epilogue: O = acc / l, lse = (m + log2 l) ln 2 (LDS now holds the staging rows)
+  uint16_t* og = static_cast<uint16_t*>(p.o);
+  const int rows_valid = max(0, min(32, p.Lq - wr0));
+  const float lt = pair_sum(l);
+  const bool any = (lt > 0.f) && (m != -INFINITY);
+  const float inv = any ? 1.f / lt : 0.f;
+  const float lse = any ? (m + log2f(lt)) * kLn2 : -INFINITY;
+  if constexpr (!kRing) {
+    if (og) store_rows_bf16(stage_w, acc, inv, og + b * p.so.b + hh * p.so.h + wr0 * p.so.l, p.so.l, rows_valid);
+    if (p.lse && h32 == 0 && qrow < p.Lq) p.lse[((int64_t)b * p.H + hh) * p.Lq + qrow] = lse;
+  } else {
+    float* lag = p.lse_acc + ((int64_t)b * p.H + hh) * p.Lq;
+    float* oag = p.o_acc + b * p.soa.b + hh * p.soa.h + wr0 * p.soa.l;
+    uint16_t* ofg = og ? og + b * p.so.b + hh * p.so.h + wr0 * p.so.l : nullptr;
+    if (ntiles > 0) {
+      // a row that saw nothing new keeps its state bit for bit
+      const bool untouched = (m == m_init) && (lt == 1.f);
+      const float sc = untouched ? 1.f : inv;
+      store_rows_f32(stage_w, acc, sc, oag, p.soa.l, rows_valid);
+      if (h32 == 0 && qrow < p.Lq && !untouched) lag[qrow] = lse;
+      if (ofg) store_rows_bf16(stage_w, acc, sc, ofg, p.so.l, rows_valid);
+    } else if (ofg) {
+      // nothing visible in this shard for the whole tile: the bf16 copy is the state itself
+      f32x16 tmp[4];
+      load_rows_f32(stage_w, tmp, oag, p.soa.l, rows_valid);
+      store_rows_bf16(stage_w, tmp, 1.f, ofg, p.so.l, rows_valid);
     }
   }
 }
@@ -512,10 +533,16 @@ static_assert(sizeof(SmemF32) >= kWaves * 32 * D * 4, "epilogue staging must fit
 hipError_t launch_attn_fwd(const FwdParams& p, bool bf16, hipStream_t stream) {
   if (p.Lq == 0 || p.B == 0 || p.H == 0) return hipSuccess;
   if (bf16) {
-    constexpr int QB = 1, BM = kWaves * 32 * QB;
-    const int nqt = (p.Lq + BM - 1) / BM;
-    LWM_LAUNCH(p.mode == 1 ? "ring_step_bf16" : "attn_fwd_bf16", attn_fwd_bf16_kernel<QB>, dim3(nqt * p.B * p.H),
-               dim3(kThreads), stream, p);
+    const int nqt = (p.Lq + kWaves * 32 - 1) / (kWaves * 32);
+    const dim3 grid(nqt * p.B * p.H), block(kThreads);
+    const bool segs = p.seg_q != nullptr;
+    if (p.mode == 1) {
+      if (segs) LWM_LAUNCH("ring_step_bf16", (attn_fwd_bf16_kernel<true, true>), grid, block, stream, p);
+      else LWM_LAUNCH("ring_step_bf16", (attn_fwd_bf16_kernel<false, true>), grid, block, stream, p);
+    } else {
+      if (segs) LWM_LAUNCH("attn_fwd_bf16", (attn_fwd_bf16_kernel<true, false>), grid, block, stream, p);
+      else LWM_LAUNCH("attn_fwd_bf16", (attn_fwd_bf16_kernel<false, false>), grid, block, stream, p);
+    }
   } else {
     const int nqt = (p.Lq + 127) / 128;
     LWM_LAUNCH("attn_fwd_f32", attn_fwd_f32_kernel, dim3(nqt * p.B * p.H), dim3(kThreads), stream, p);
