@@ -358,12 +358,15 @@ __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams 
     if (w == 1) load_lds4(make_rsrc(dlt_row + q0, rem), &sm.dlt[st][0], lane * 4);
     if (segs && w == 2) load_lds4(make_rsrc(segq_row + q0, rem), &sm.seg[st][0], lane * 4);
   };
-  int roff[8];  // row-major operand (Q, dO, K, V rows) for feature step sd
-#pragma unroll
-  for (int sd = 0; sd < 8; ++sd) roff[sd] = rm_offset(c32, 2 * sd + h32);
-  int tlo[4], thi[4];  // Q^T / dO^T operand for feature block db (+4096 per 16-query group)
-#pragma unroll
-  for (int db = 0; db < 4; ++db) tr_offsets(lane, db, tlo[db], thi[db]);
+  // Row-major operand (Q, dO, K, V rows; row c32 within its 32-row block, chunk 2*sd + h32): the
+  // XOR swizzle leaves bit 0 of an even chunk index alone, so the offset is a per-lane base plus
+  // ((2*sd) ^ swizzle) * 16.  Transposing reads (Q^T, dO^T) for feature block db differ from block
+  // 0's offsets by an XOR of db into chunk bits 2..3.
+  const int rswz = swz16(c32 & 15);
+  const int rbase = c32 * 256 + (((h32 ^ rswz) & 1) << 4);
+  auto roff = [&](int sd) { return rbase + (((2 * sd) ^ (rswz & 14)) << 4); };
+  int tlo0, thi0;
+  tr_offsets(lane, 0, tlo0, thi0);
 
   if (ntiles > 0) issue(t_begin, 0);
   for (int it = 0; it < ntiles; ++it) {
@@ -388,16 +391,29 @@ __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams 
     }
     if (!active) continue;
 
-    // S = Q K^T and dP = dO V^T (32 queries x 32 keys)
+    // S = Q K^T and dP = dO V^T (32 queries x 32 keys); the four operand fragments of feature
+    // step sd + 1 are read while the two MFMAs of step sd run
     f32x16 s, dp;
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+    {
+      bf16x8 f[2][4];
+      auto rd = [&](int sd, bf16x8 (&d)[4]) {
+        const int o = roff(sd);
+        d[0] = as_bf16x8(*reinterpret_cast<const u32x4*>(qt + o));
+        d[1] = as_bf16x8(*reinterpret_cast<const u32x4*>(kw + o));
+        d[2] = as_bf16x8(*reinterpret_cast<const u32x4*>(ot + o));
+        d[3] = as_bf16x8(*reinterpret_cast<const u32x4*>(vw + o));
+      };
+      rd(0, f[0]);
 #pragma unroll
-    for (int sd = 0; sd < 8; ++sd) {
-      s = mfma_32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(qt + roff[sd])),
-                        as_bf16x8(*reinterpret_cast<const u32x4*>(kw + roff[sd])), s);
-      dp = mfma_32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(ot + roff[sd])),
-                         as_bf16x8(*reinterpret_cast<const u32x4*>(vw + roff[sd])), dp);
+      for (int sd = 0; sd < 8; ++sd) {
+        if (sd + 1 < 8) rd(sd + 1, f[(sd + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        s = mfma_32x32x16(f[sd & 1][0], f[sd & 1][1], s);
+        dp = mfma_32x32x16(f[sd & 1][2], f[sd & 1][3], dp);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     // lane owns key krow; element i is query wq0 + acc_row(i, h32)
 #pragma unroll
@@ -413,13 +429,21 @@ __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams 
       }
     }
     if (need_mask) {
-      // masked scores get exponent -inf (a select, not a branch): exp2(-inf) = 0
+      // element i holds query ql = qh*32 + 8*(i/4) + 4*h32 + i%4, visible iff ql >= lo (causal)
+      // and its segment matches this lane's key; masked scores get exponent -inf (a select)
+      int lo = -BQ;
+      if (p.causal) lo = (int)imax64(-BQ, imin64(BQ, gk - p.q_offset - q0));
+      lo -= qh * 32 + 4 * h32;
+      const int32_t* segt = &sm.seg[st][qh * 32 + 4 * h32];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int ql = qh * 32 + acc_row(i, h32);
-        const int32_t qs = segs ? sm.seg[st][ql] : myseg;
-        const bool vis = (!p.causal | (gk <= p.q_offset + q0 + ql)) & (qs == myseg);
-        s[i] = vis ? s[i] : -INFINITY;
+      for (int g = 0; g < 4; ++g) {
+        i32x4 qs = {myseg, myseg, myseg, myseg};
+        if (segs) qs = *reinterpret_cast<const i32x4*>(segt + 8 * g);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bool vis = (8 * g + j >= lo) & (qs[j] == myseg);
+          s[4 * g + j] = vis ? s[4 * g + j] : -INFINITY;
+        }
       }
     }
 #pragma unroll
@@ -429,12 +453,24 @@ __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams 
     }
     const bf16x8 pb[2] = {pack8(s, 0), pack8(s, 1)};
     const bf16x8 dsb[2] = {pack8(dp, 0), pack8(dp, 1)};
-    // dV^T += dO^T P, dK^T += Q^T dS (transposed operands by transposing reads)
+    // dV^T += dO^T P, dK^T += Q^T dS (transposed operands by transposing reads, one step ahead)
+    {
+      bf16x8 g[2][2];
+      auto rdt = [&](int n, bf16x8 (&d)[2]) {
+        const int u = n >> 2, db = n & 3;
+        d[0] = read_xt(ot + u * 4096, tlo0 ^ (db << 6), thi0 ^ (db << 6));
+        d[1] = read_xt(qt + u * 4096, tlo0 ^ (db << 6), thi0 ^ (db << 6));
+      };
+      rdt(0, g[0]);
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {  // n = 16-query group * 4 + feature block
-      const int u = n >> 2, db = n & 3;
-      dv[db] = mfma_32x32x16(read_xt(ot + u * 4096, tlo[db], thi[db]), pb[u], dv[db]);
-      dk[db] = mfma_32x32x16(read_xt(qt + u * 4096, tlo[db], thi[db]), dsb[u], dk[db]);
+      for (int n = 0; n < 8; ++n) {  // n = 16-query group * 4 + feature block
+        if (n + 1 < 8) rdt(n + 1, g[(n + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        const int u = n >> 2, db = n & 3;
+        dv[db] = mfma_32x32x16(g[n & 1][0], pb[u], dv[db]);
+        dk[db] = mfma_32x32x16(g[n & 1][1], dsb[u], dk[db]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
   __syncthreads();
