@@ -161,12 +161,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
     }
     if (segs && w == 0) load_lds4(make_rsrc(segk_row + k0, (int64_t)(p.Lk - k0) * 4), &sm.seg[st][0], lane * 4);
   };
-  int roff[8];  // K / V row-major operand for feature step sd (+8192 for the second key block)
-#pragma unroll
-  for (int sd = 0; sd < 8; ++sd) roff[sd] = rm_offset(c32, 2 * sd + h32);
-  int tlo[4], thi[4];  // K^T operand for feature block db (+4096 per 16-key group)
-#pragma unroll
-  for (int db = 0; db < 4; ++db) tr_offsets(lane, db, tlo[db], thi[db]);
+  // K / V row-major operand for feature step sd (+8192 for the second key block): the XOR swizzle
+  // leaves bit 0 of an even chunk index alone, so the offset is a per-lane base plus
+  // ((2*sd) ^ swizzle) * 16.  K^T operands for feature block db (+4096 per 16-key group) differ
+  // from block 0's offsets by an XOR of db into chunk bits 2..3.
+  const int rswz = swz16(c32 & 15);
+  const int rbase = c32 * 256 + (((h32 ^ rswz) & 1) << 4);
+  auto roff = [&](int sd) { return rbase + (((2 * sd) ^ (rswz & 14)) << 4); };
+  int tlo0, thi0;
+  tr_offsets(lane, 0, tlo0, thi0);
 
   if (ntiles > 0) issue(t_begin, 0);
   auto tile = [&](int st, int it) {
@@ -197,13 +200,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
       bf16x8 fk[2], fv[2];
-      fk[0] = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + kb * 8192 + roff[0]));
-      fv[0] = as_bf16x8(*reinterpret_cast<const u32x4*>(vt + kb * 8192 + roff[0]));
+      fk[0] = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + kb * 8192 + roff(0)));
+      fv[0] = as_bf16x8(*reinterpret_cast<const u32x4*>(vt + kb * 8192 + roff(0)));
 #pragma unroll
       for (int sd = 0; sd < 8; ++sd) {
         if (sd + 1 < 8) {
-          fk[(sd + 1) & 1] = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + kb * 8192 + roff[sd + 1]));
-          fv[(sd + 1) & 1] = as_bf16x8(*reinterpret_cast<const u32x4*>(vt + kb * 8192 + roff[sd + 1]));
+          fk[(sd + 1) & 1] = as_bf16x8(*reinterpret_cast<const u32x4*>(kt + kb * 8192 + roff(sd + 1)));
+          fv[(sd + 1) & 1] = as_bf16x8(*reinterpret_cast<const u32x4*>(vt + kb * 8192 + roff(sd + 1)));
         }
         __builtin_amdgcn_sched_barrier(0);
         s = mfma_32x32x16(fk[sd & 1], qreg[sd], s);
@@ -215,13 +218,21 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) x[i] = __builtin_fmaf(s[i], p.scale_log2, -lse2);
       if (need_mask) {
+        // element i holds tile key kl = kb*32 + 8*(i/4) + 4*h32 + i%4, visible iff kl < lim (end of
+        // the keys, causal limit) and its segment matches this lane's query
+        int64_t lim64 = (int64_t)p.Lk - k0;
+        if (p.causal) lim64 = imin64(lim64, gq - p.k_offset - k0 + 1);
+        const int lim = (int)imax64(imin64(lim64, BN), 0) - kb * 32 - 4 * h32;
+        const int32_t* segt = &sm.seg[st][kb * 32 + 4 * h32];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kl = kb * 32 + acc_row(i, h32);
-          const int key = k0 + kl;
-          const int32_t ks = segs ? sm.seg[st][kl] : myseg;
-          const bool vis = (key < p.Lk) & (!p.causal | (p.k_offset + key <= gq)) & (ks == myseg);
-          x[i] = vis ? x[i] : -INFINITY;
+        for (int g = 0; g < 4; ++g) {
+          i32x4 ks = {myseg, myseg, myseg, myseg};
+          if (segs) ks = *reinterpret_cast<const i32x4*>(segt + 8 * g);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bool vis = (8 * g + j < lim) & (ks[j] == myseg);
+            x[4 * g + j] = vis ? x[4 * g + j] : -INFINITY;
+          }
         }
       }
 #pragma unroll
@@ -232,7 +243,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
     // dQ^T += K^T dS^T (K^T operands by transposing reads, two ahead)
     {
       bf16x8 kf[3];
-      auto kread = [&](int n) { return read_xt(kt + (n >> 2) * 4096, tlo[n & 3], thi[n & 3]); };
+      auto kread = [&](int n) { return read_xt(kt + (n >> 2) * 4096, tlo0 ^ ((n & 3) << 6), thi0 ^ ((n & 3) << 6)); };
       kf[0] = kread(0);
       kf[1] = kread(1);
 #pragma unroll
