@@ -379,13 +379,17 @@ __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams 
   int tlo0, thi0;
   tr_offsets(lane, 0, tlo0, thi0);
 
-  if (ntiles > 0) issue(t_begin, 0);
+  // Query tiles are visited from the last one down: every workgroup of a head then starts on the
+  // same tile and they move through Q and dO together, so each tile is fetched into L2 once and
+  // read there by all of them.
+  const int t_last = t_begin + ntiles - 1;
+  if (ntiles > 0) issue(t_last, 0);
   for (int it = 0; it < ntiles; ++it) {
     const int st = it & 1;
-    const int q0 = (t_begin + it) * BQ;
+    const int q0 = (t_last - it) * BQ;
     wait_vmcnt<0>();
     __syncthreads();
-    if (it + 1 < ntiles) issue(t_begin + it + 1, st ^ 1);
+    if (it + 1 < ntiles) issue(t_last - it - 1, st ^ 1);
     const uint8_t* qt = sm.qo[st][0] + qh * 8192;  // this wave's 32 queries
     const uint8_t* ot = sm.qo[st][1] + qh * 8192;
     const int wq0 = q0 + qh * 32;
