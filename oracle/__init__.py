@@ -11,6 +11,7 @@ from .attention import (  # noqa: F401
     inv_freq,
     merge,
     positions,
+    ring_step_bwd,
     rope,
     segment_positions,
     training_step,

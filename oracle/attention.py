@@ -252,6 +252,67 @@ def attention_bwd(q, k, v, dout, seg_q=None, seg_k=None, q_offset: int = 0, k_of
 
 
 # ----------------------------------------------------------------------------------------
+# Backward ring step ([LWM-blog] §3.1: each device keeps its query block while key/value
+# blocks travel the ring; for the backward the gradients of a key/value block travel with it)
+# ----------------------------------------------------------------------------------------
+def ring_step_bwd(q, k, v, o, lse, dout, seg_q=None, seg_k=None, q_offset: int = 0, k_offset: int = 0,
+                  causal: bool = True, scale: float | None = None, row_block: int = 512,
+                  threads: int | None = None):
+    """Contributions of one key/value shard to the gradients of sum(dout * O), float64.
+
+    O [B, Lq, H, D] and lse [B, H, Lq] are the forward's final results over *all* shards, so
+    P_ij = exp(S_ij * scale - lse_i) on this shard's visible keys is the exact probability and
+    D_i = sum_d dO_id O_id is the full row term.  Returns (dq, dk, dv): dq [B, Lq, H, D] is this
+    shard's share of dQ (summed over shards it gives dQ), dk / dv [B, Lk, H, D] are this query
+    block's share of the shard's dK / dV (summed over query blocks they give dK / dV).
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    o = np.asarray(o)
+    lse = np.asarray(lse)
+    dout = np.asarray(dout)
+    B, Lq, H, D = q.shape
+    Lk = k.shape[1]
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    dq = np.zeros((B, Lq, H, D), dtype=np.float64)
+    dk = np.zeros((B, Lk, H, D), dtype=np.float64)
+    dv = np.zeros((B, Lk, H, D), dtype=np.float64)
+
+    def one(task):
+        b, h = task
+        kh = np.ascontiguousarray(k[b, :, h, :], dtype=np.float64)
+        vh = np.ascontiguousarray(v[b, :, h, :], dtype=np.float64)
+        dkh = np.zeros((Lk, D))
+        dvh = np.zeros((Lk, D))
+        for r0 in range(0, Lq, row_block):
+            rr = np.arange(r0, min(Lq, r0 + row_block))
+            lim = _key_limit(rr, Lk, q_offset, k_offset, causal)
+            if lim == 0:
+                continue
+            qb = np.asarray(q[b, rr, h, :], dtype=np.float64)
+            dob = np.asarray(dout[b, rr, h, :], dtype=np.float64)
+            ob = np.asarray(o[b, rr, h, :], dtype=np.float64)
+            lb = np.asarray(lse[b, h, rr], dtype=np.float64)
+            vis = visible(rr, lim, q_offset, k_offset, causal,
+                          None if seg_q is None else seg_q[b], None if seg_k is None else seg_k[b][:lim])
+            s = (qb @ kh[:lim].T) * scale
+            has = np.isfinite(lb)
+            p = np.where(vis & has[:, None], np.exp(s - np.where(has, lb, 0.0)[:, None]), 0.0)
+            d_i = np.sum(dob * ob, axis=1)
+            dvh[:lim] += p.T @ dob
+            dp = dob @ vh[:lim].T
+            ds = p * (dp - d_i[:, None])
+            dq[b, rr, h, :] = scale * (ds @ kh[:lim])
+            dkh[:lim] += scale * (ds.T @ qb)
+        dk[b, :, h, :] = dkh
+        dv[b, :, h, :] = dvh
+
+    _pool_map(one, [(b, h) for b in range(B) for h in range(H)], _threads(threads))
+    return dq, dk, dv
+
+
+# ----------------------------------------------------------------------------------------
 # Merge of two partial results over disjoint key sets (ring step; [LWM-blog] §3.1 rotates
 # KV blocks around the ring, each visit contributes one partial softmax)
 # ----------------------------------------------------------------------------------------

@@ -357,6 +357,44 @@ def pin_backward_identities(orc):
         assert abs(np.sum(dv[:, :, h] * v[:, :, h]) - np.sum(do[:, :, h] * o[:, :, h])) < 1e-10
 
 
+def pin_ring_backward(orc):
+    """Backward ring: per-shard contributions under the final (O, lse) sum to torch.autograd's
+    gradients through SDPA (CPU float64) over all keys; a shard wholly in the future adds zero."""
+    import torch
+    import torch.nn.functional as F
+    rng = _rng(23)
+    B, Lq, H, D = 1, 40, 2, 8
+    n_shards, shard = 6, 24
+    Lk = n_shards * shard
+    q_off = 3 * shard + 5
+    q, do = _rand(rng, B, Lq, H, D), _rand(rng, B, Lq, H, D)
+    k, v = _rand(rng, B, Lk, H, D), _rand(rng, B, Lk, H, D)
+    ids = np.repeat(np.arange(5), [30, 17, 41, 9, 47])[None, :]     # packed row, global coordinates
+    seg_q, seg_k = ids[:, q_off:q_off + Lq], ids[:, :Lk]
+    gq = np.arange(Lq) + q_off
+    mask = (np.arange(Lk)[None, :] <= gq[:, None]) & (seg_q[0][:, None] == seg_k[0][None, :])
+    assert mask.any(axis=1).all()
+    tq, tk, tv = (torch.tensor(np.transpose(a, (0, 2, 1, 3)), requires_grad=True) for a in (q, k, v))
+    tmask = torch.from_numpy(mask)[None, None]
+    out = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=tmask)
+    out.backward(torch.from_numpy(np.ascontiguousarray(np.transpose(do, (0, 2, 1, 3)))))
+    scores = (tq.detach() @ tk.detach().transpose(-1, -2)) / math.sqrt(D)
+    lse = torch.logsumexp(scores.masked_fill(~tmask, -math.inf), dim=-1).numpy()       # [B, H, Lq]
+    o = np.transpose(out.detach().numpy(), (0, 2, 1, 3))
+    ref_dq, ref_dk, ref_dv = (np.transpose(t.grad.numpy(), (0, 2, 1, 3)) for t in (tq, tk, tv))
+    dq_sum = np.zeros_like(q)
+    for j in (3, 2, 1, 0, 5, 4):                                     # ring order from the home shard
+        sl = slice(j * shard, (j + 1) * shard)
+        dq_j, dk_j, dv_j = orc.ring_step_bwd(q, k[:, sl], v[:, sl], o, lse, do, seg_q, seg_k[:, sl],
+                                             q_off, j * shard, True, None, threads=1)
+        dq_sum += dq_j
+        assert np.allclose(dk_j, ref_dk[:, sl], atol=1e-11, rtol=0), j
+        assert np.allclose(dv_j, ref_dv[:, sl], atol=1e-11, rtol=0), j
+        if j == 5:                                                   # keys 120.. are all in the future
+            assert not np.any(dq_j) and not np.any(dk_j) and not np.any(dv_j)
+    assert np.allclose(dq_sum, ref_dq, atol=1e-11, rtol=0)
+
+
 def pin_training_step_autograd(orc):
     """Gradients w.r.t. pre-RoPE Q, K: RoPE as complex multiplication + SDPA under autograd."""
     import torch
@@ -408,5 +446,5 @@ ALL_PINS = [
     pin_forward_brute_force, pin_forward_sdpa, pin_forward_closed_forms, pin_forward_invariants,
     pin_packed_equals_unpacked, pin_block_and_ring_invariance, pin_rope, pin_segment_positions,
     pin_backward_finite_differences, pin_backward_autograd, pin_backward_identities,
-    pin_training_step_autograd, pin_golden,
+    pin_training_step_autograd, pin_ring_backward, pin_golden,
 ]

@@ -35,6 +35,9 @@ MUTANTS = [
     ("merge_weights_swapped", "return ca * np.asarray(o_a, dtype=np.float64) + cb * np.asarray(o_b",
      "return cb * np.asarray(o_a, dtype=np.float64) + ca * np.asarray(o_b"),
     ("segment_positions_not_restarting", "                start = t\n", "                start = 0\n"),
+    ("ring_bwd_lse_not_subtracted", "np.exp(s - np.where(has, lb, 0.0)[:, None])", "np.exp(s)"),
+    ("ring_bwd_rowsum_from_zero_o", "ob = np.asarray(o[b, rr, h, :], dtype=np.float64)", "ob = np.zeros_like(dob)"),
+    ("ring_bwd_mask_ignored", "p = np.where(vis & has[:, None],", "p = np.where(has[:, None],"),
     ("training_inverse_rope_forgotten", "dq = rope(dqr, pos_q, theta, layout, inverse=True)",
      "dq = rope(dqr, pos_q, theta, layout)"),
 ]
