@@ -194,7 +194,32 @@ def bench_extras(torch, lwm, path, workloads, configs, steps=3, warmup=1):
                    "ring_kernel_tflops": w.fwd_flop() / rk["ms_per_step"] / 1e9,
                    "pct_of_bf16_peak": 100 * w.fwd_flop() / rk["ms_per_step"] / 1e9 / configs.PEAK_BF16_TFLOPS,
                    "query_tokens_per_s": w.B * S / (ms * 1e-3), "kernels": ks}
-    del d, qr, kr, o_acc, lse_acc, o
+
+    # the same share's backward ring: the 41 shards visit again, each adding its share of the
+    # gradients (dQ stays, dK / dV travel with their shard); o / lse_acc hold the forward's result
+    f32 = dict(dtype=torch.float32, device="cuda")
+    dq_acc = torch.empty((w.B, S, w.H, w.D), **f32)
+    dk_acc = {j: torch.empty((w.B, S, w.H, w.D), **f32) for j in kr}
+    dv_acc = {j: torch.empty((w.B, S, w.H, w.D), **f32) for j in kr}
+    ws = torch.empty(lwm.lwm_blockattn_bwd_workspace_size(w.B, w.H, S, S, w.D), dtype=torch.uint8, device="cuda")
+
+    def ring_bwd_step():
+        for t in (dq_acc, *dk_acc.values(), *dv_acc.values()):
+            t.zero_()
+        path.ring_backward(qr, kr, d["v_shards"], o, lse_acc, d["do"], w.ring_order(), S, w.q_offset,
+                           dq_acc=dq_acc, dk_acc=dk_acc, dv_acc=dv_acc, workspace=ws)
+
+    ms, prof = time_steps(ring_bwd_step, steps, warmup, lwm, torch)
+    ks = kernels_table(prof, steps)
+    kms = sum(ks[k]["ms_per_step"] for k in ("bwd_delta", "bwd_dq", "bwd_dkdv") if k in ks)
+    bflop = 10 * w.D * w.visible_pairs()
+    out[w.name + "_backward"] = {
+        "ms_per_step": ms, "ring_steps_per_pass": ks["bwd_dkdv"]["launches_per_step"],
+        "kernel_ms_per_pass": kms, "tflops": bflop / ms / 1e9, "kernel_tflops": bflop / kms / 1e9,
+        "pct_of_bf16_peak": 100 * bflop / kms / 1e9 / configs.PEAK_BF16_TFLOPS,
+        "note": "10*D flop per visible pair; ms_per_step also zeroes the float32 accumulators",
+        "kernels": ks}
+    del d, qr, kr, o_acc, lse_acc, o, dq_acc, dk_acc, dv_acc, ws
     torch.cuda.empty_cache()
     return out
 

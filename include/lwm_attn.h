@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define LWM_ABI_VERSION 1
+#define LWM_ABI_VERSION 2
 
 typedef enum {
   LWM_OK = 0,
@@ -155,6 +155,32 @@ int lwm_ring_step(const lwm_tensor4* q, const lwm_tensor4* k_shard, const lwm_te
                   const int32_t* seg_q, const int32_t* seg_k, int64_t q_offset, int64_t k_offset,
                   int32_t causal, float scale, const lwm_tensor4* o_acc, float* lse_acc,
                   const lwm_tensor4* o_final, void* stream);
+
+/*
+ * Backward ring step (bf16): add one KV shard's share of the gradients.  On the pages the
+ * sequence is cut into blocks held by devices in a ring, each device computing on one block
+ * while the next one arrives ("开源巨兽LWM：如何用RingAttention撬动百万Token多模态世界", section
+ * 3.1); in the backward pass the query block (with its dout, O and lse) stays and each visiting
+ * KV shard picks up this block's contribution to its dK, dV on the way:
+ *     P = exp(scale Q K_shard^T - lse) on the shard's visible keys,  D_i = sum_d dout_id O_id,
+ *     dq_acc += scale dS K_shard,  dk_acc += scale dS^T Q,  dv_acc += P^T dout,
+ * with dS = P o (dout V_shard^T - D).  o and lse must be the forward's results over *all*
+ * shards (e.g. lwm_ring_step's final state), so summing the steps over every shard gives
+ * exactly lwm_blockattn_bwd's gradients.  q, dout, o: bf16 [B, Lq, H, 128]; k_shard, v_shard:
+ * bf16 [B, Lk, H, 128]; k_offset is the global index of the shard's first key; seg_*, causal,
+ * scale as in lwm_blockattn_fwd.  dq_acc (like q) and dk_acc, dv_acc (like k_shard) are
+ * float32 lwm_tensor4 views that are read and added to (the caller zeroes them before the first
+ * step); results are w.r.t. the rotated operands, as for lwm_blockattn_bwd.  workspace: at
+ * least lwm_blockattn_bwd_workspace_size(B, H, Lq, Lk, D) bytes, 256-byte aligned (D and the
+ * rescaled lse are recomputed into it on every call).  Errors as for lwm_blockattn_bwd; a
+ * shard wholly in the causal future adds zero.
+ */
+int lwm_ring_step_bwd(const lwm_tensor4* q, const lwm_tensor4* k_shard, const lwm_tensor4* v_shard,
+                      const lwm_tensor4* o, const float* lse, const lwm_tensor4* dout,
+                      const int32_t* seg_q, const int32_t* seg_k, int64_t q_offset,
+                      int64_t k_offset, int32_t causal, float scale, const lwm_tensor4* dq_acc,
+                      const lwm_tensor4* dk_acc, const lwm_tensor4* dv_acc, void* workspace,
+                      size_t workspace_bytes, void* stream);
 
 /*
  * Kernel timing (instrumentation, not part of the method).  While enabled, every kernel the

@@ -158,19 +158,21 @@ size_t lwm_blockattn_bwd_workspace_size(int64_t B, int64_t H, int64_t Lq, int64_
   return 2 * ((rows + 255) / 256 * 256);  // delta, then lse * log2(e)
 }
 
-int lwm_blockattn_bwd(const lwm_tensor4* q, const lwm_tensor4* k, const lwm_tensor4* v, const lwm_tensor4* o,
-                      const float* lse, const lwm_tensor4* dout, const int32_t* seg_q, const int32_t* seg_k,
-                      int64_t q_offset, int64_t k_offset, int32_t causal, float scale, const lwm_tensor4* dq,
-                      const lwm_tensor4* dk, const lwm_tensor4* dv, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the backward and the backward ring step; fills every parameter but the
+// gradient outputs.
+int prepare_bwd(const lwm_tensor4* q, const lwm_tensor4* k, const lwm_tensor4* v, const lwm_tensor4* o,
+                const float* lse, const lwm_tensor4* dout, const int32_t* seg_q, const int32_t* seg_k,
+                int64_t q_offset, int64_t k_offset, int32_t causal, float scale, void* workspace,
+                size_t workspace_bytes, lwm::BwdParams* p) {
   int s;
   if ((s = check_attention(q, k, v, seg_q, seg_k, q_offset, k_offset, causal))) return s;
   if (q->dtype != LWM_BF16) return fail(LWM_ERR_UNSUPPORTED, "backward is implemented for bf16 only");
   if ((s = check_tensor(o, "o")) || (s = check_same(q, o, "q", "o", true))) return s;
   if ((s = check_tensor(dout, "dout")) || (s = check_same(q, dout, "q", "dout", true))) return s;
-  if ((s = check_tensor(dq, "dq")) || (s = check_same(q, dq, "q", "dq", true))) return s;
-  if ((s = check_tensor(dk, "dk")) || (s = check_same(k, dk, "k", "dk", true))) return s;
-  if ((s = check_tensor(dv, "dv")) || (s = check_same(v, dv, "v", "dv", true))) return s;
   float sc;
   if ((s = check_scale(scale, q->D, &sc))) return s;
   const bool empty = q->B == 0 || q->H == 0 || (q->L == 0 && k->L == 0);
@@ -179,26 +181,76 @@ int lwm_blockattn_bwd(const lwm_tensor4* q, const lwm_tensor4* k, const lwm_tens
   if (!empty && (!workspace || workspace_bytes < need))
     return fail(LWM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
   if (workspace && reinterpret_cast<uintptr_t>(workspace) % 256) return fail(LWM_ERR_WORKSPACE, "workspace not 256-byte aligned");
-  lwm::BwdParams p{};
-  p.q = static_cast<const uint16_t*>(q->ptr);
-  p.k = static_cast<const uint16_t*>(k->ptr);
-  p.v = static_cast<const uint16_t*>(v->ptr);
-  p.o = static_cast<const uint16_t*>(o->ptr);
-  p.dout = static_cast<const uint16_t*>(dout->ptr);
-  p.sq = strides(q); p.sk = strides(k); p.sv = strides(v); p.so = strides(o); p.sdo = strides(dout);
-  p.lse = lse;
-  p.delta = static_cast<float*>(workspace);
-  p.lse2 = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) + need / 2) : nullptr;
-  p.B = (int)q->B; p.H = (int)q->H; p.Lq = (int)q->L; p.Lk = (int)k->L;
-  p.seg_q = seg_q; p.seg_k = seg_k;
-  p.q_offset = q_offset; p.k_offset = k_offset; p.causal = causal;
-  p.scale = sc;
-  p.scale_log2 = sc * 1.4426950408889634f;
+  *p = lwm::BwdParams{};
+  p->q = static_cast<const uint16_t*>(q->ptr);
+  p->k = static_cast<const uint16_t*>(k->ptr);
+  p->v = static_cast<const uint16_t*>(v->ptr);
+  p->o = static_cast<const uint16_t*>(o->ptr);
+  p->dout = static_cast<const uint16_t*>(dout->ptr);
+  p->sq = strides(q); p->sk = strides(k); p->sv = strides(v); p->so = strides(o); p->sdo = strides(dout);
+  p->lse = lse;
+  p->delta = static_cast<float*>(workspace);
+  p->lse2 = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) + need / 2) : nullptr;
+  p->B = (int)q->B; p->H = (int)q->H; p->Lq = (int)q->L; p->Lk = (int)k->L;
+  p->seg_q = seg_q; p->seg_k = seg_k;
+  p->q_offset = q_offset; p->k_offset = k_offset; p->causal = causal;
+  p->scale = sc;
+  p->scale_log2 = sc * 1.4426950408889634f;
+  return LWM_OK;
+}
+
+// A float32 gradient accumulator with the shape of `like` (q for dQ, k for dK and dV).
+int check_acc(const lwm_tensor4* acc, const lwm_tensor4* like, const char* name) {
+  int s;
+  if ((s = check_tensor(acc, name))) return s;
+  if (acc->dtype != LWM_FP32) return fail(LWM_ERR_INVALID_ARG, "%s must be float32", name);
+  if (acc->B != like->B || acc->L != like->L || acc->H != like->H || acc->D != like->D)
+    return fail(LWM_ERR_INVALID_ARG, "%s: shape mismatch", name);
+  return LWM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lwm_blockattn_bwd(const lwm_tensor4* q, const lwm_tensor4* k, const lwm_tensor4* v, const lwm_tensor4* o,
+                      const float* lse, const lwm_tensor4* dout, const int32_t* seg_q, const int32_t* seg_k,
+                      int64_t q_offset, int64_t k_offset, int32_t causal, float scale, const lwm_tensor4* dq,
+                      const lwm_tensor4* dk, const lwm_tensor4* dv, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  lwm::BwdParams p;
+  int s;
+  if ((s = prepare_bwd(q, k, v, o, lse, dout, seg_q, seg_k, q_offset, k_offset, causal, scale, workspace,
+                       workspace_bytes, &p)))
+    return s;
+  if ((s = check_tensor(dq, "dq")) || (s = check_same(q, dq, "q", "dq", true))) return s;
+  if ((s = check_tensor(dk, "dk")) || (s = check_same(k, dk, "k", "dk", true))) return s;
+  if ((s = check_tensor(dv, "dv")) || (s = check_same(v, dv, "v", "dv", true))) return s;
   p.dq = static_cast<uint16_t*>(dq->ptr);
   p.dk = static_cast<uint16_t*>(dk->ptr);
   p.dv = static_cast<uint16_t*>(dv->ptr);
   p.sdq = strides(dq); p.sdk = strides(dk); p.sdv = strides(dv);
   return hip_status(lwm::launch_attn_bwd(p, static_cast<hipStream_t>(stream)), "backward launch");
+}
+
+int lwm_ring_step_bwd(const lwm_tensor4* q, const lwm_tensor4* k_shard, const lwm_tensor4* v_shard,
+                      const lwm_tensor4* o, const float* lse, const lwm_tensor4* dout, const int32_t* seg_q,
+                      const int32_t* seg_k, int64_t q_offset, int64_t k_offset, int32_t causal, float scale,
+                      const lwm_tensor4* dq_acc, const lwm_tensor4* dk_acc, const lwm_tensor4* dv_acc,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  lwm::BwdParams p;
+  int s;
+  if ((s = prepare_bwd(q, k_shard, v_shard, o, lse, dout, seg_q, seg_k, q_offset, k_offset, causal, scale, workspace,
+                       workspace_bytes, &p)))
+    return s;
+  if ((s = check_acc(dq_acc, q, "dq_acc")) || (s = check_acc(dk_acc, k_shard, "dk_acc")) ||
+      (s = check_acc(dv_acc, k_shard, "dv_acc")))
+    return s;
+  p.dq_acc = static_cast<float*>(dq_acc->ptr);
+  p.dk_acc = static_cast<float*>(dk_acc->ptr);
+  p.dv_acc = static_cast<float*>(dv_acc->ptr);
+  p.sdqa = strides(dq_acc); p.sdka = strides(dk_acc); p.sdva = strides(dv_acc);
+  return hip_status(lwm::launch_attn_bwd(p, static_cast<hipStream_t>(stream)), "backward ring step launch");
 }
 
 int lwm_ring_step(const lwm_tensor4* q, const lwm_tensor4* k_shard, const lwm_tensor4* v_shard, const int32_t* seg_q,

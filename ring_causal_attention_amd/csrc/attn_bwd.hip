@@ -75,7 +75,7 @@ struct SmemDq {
   uint8_t kv[2][2][kTileBytes];  // [stage][K, V] row-major swizzled
   int32_t seg[2][64];
 };
-static_assert(sizeof(SmemDq) >= kWaves * 32 * D * 2, "epilogue staging must fit");
+static_assert(sizeof(SmemDq) >= kWaves * 32 * D * 4, "epilogue staging (float32 rows) must fit");
 
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
   constexpr int MW = 32, BM = kWaves * MW, BN = 64;
@@ -258,9 +258,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
   };
   for (int it = 0; it < ntiles; ++it) tile(it & 1, it);
   __syncthreads();
-  uint8_t* stage_w = reinterpret_cast<uint8_t*>(&sm) + w * (32 * D * 2);
-  store_rows_bf16(stage_w, acc, p.scale, p.dq + b * p.sdq.b + hh * p.sdq.h + wr0 * p.sdq.l, p.sdq.l,
-                  max(0, min(32, p.Lq - wr0)));
+  const int rows_valid = max(0, min(32, p.Lq - wr0));
+  if (p.dq_acc) {  // backward ring step: dQ += this shard's share, in float32
+    uint8_t* stage_w = reinterpret_cast<uint8_t*>(&sm) + w * (32 * D * 4);
+    add_rows_f32(stage_w, acc, p.scale, p.dq_acc + b * p.sdqa.b + hh * p.sdqa.h + wr0 * p.sdqa.l, p.sdqa.l,
+                 rows_valid);
+  } else {
+    uint8_t* stage_w = reinterpret_cast<uint8_t*>(&sm) + w * (32 * D * 2);
+    store_rows_bf16(stage_w, acc, p.scale, p.dq + b * p.sdq.b + hh * p.sdq.h + wr0 * p.sdq.l, p.sdq.l, rows_valid);
+  }
 }
 
 // ------------------------------------------------------------------------------ dK / dV
@@ -279,6 +285,7 @@ struct SmemDkdv {
   int32_t seg[2][BQ];
 };
 static_assert(sizeof(SmemDkdv) >= 4 * 32 * D * 4 * 2, "partial-sum exchange must fit");
+static_assert(sizeof(SmemDkdv) >= kDkdvWaves * 32 * D * 4, "epilogue staging (float32 rows) must fit");
 
 __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int BK = 128;
@@ -516,11 +523,17 @@ __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams 
       }
   }
   __syncthreads();
-  // waves 0..3 store (store_rows_bf16 has block-wide barriers: every wave takes part)
-  uint8_t* stage_w = reinterpret_cast<uint8_t*>(&sm) + w * (32 * D * 2);
+  // waves 0..3 store (the row helpers have block-wide barriers: every wave takes part)
   const int rows_valid = qh == 0 ? max(0, min(32, p.Lk - wk0)) : 0;
-  store_rows_bf16(stage_w, dk, p.scale, p.dk + b * p.sdk.b + hh * p.sdk.h + wk0 * p.sdk.l, p.sdk.l, rows_valid);
-  store_rows_bf16(stage_w, dv, 1.f, p.dv + b * p.sdv.b + hh * p.sdv.h + wk0 * p.sdv.l, p.sdv.l, rows_valid);
+  if (p.dk_acc) {  // backward ring step: dK, dV += this query block's share, in float32
+    uint8_t* stage_w = reinterpret_cast<uint8_t*>(&sm) + w * (32 * D * 4);
+    add_rows_f32(stage_w, dk, p.scale, p.dk_acc + b * p.sdka.b + hh * p.sdka.h + wk0 * p.sdka.l, p.sdka.l, rows_valid);
+    add_rows_f32(stage_w, dv, 1.f, p.dv_acc + b * p.sdva.b + hh * p.sdva.h + wk0 * p.sdva.l, p.sdva.l, rows_valid);
+  } else {
+    uint8_t* stage_w = reinterpret_cast<uint8_t*>(&sm) + w * (32 * D * 2);
+    store_rows_bf16(stage_w, dk, p.scale, p.dk + b * p.sdk.b + hh * p.sdk.h + wk0 * p.sdk.l, p.sdk.l, rows_valid);
+    store_rows_bf16(stage_w, dv, 1.f, p.dv + b * p.sdv.b + hh * p.sdv.h + wk0 * p.sdv.l, p.sdv.l, rows_valid);
+  }
 }
 
 }  // namespace

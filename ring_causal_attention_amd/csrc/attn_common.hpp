@@ -211,6 +211,19 @@ __device__ inline void load_rows_f32(uint8_t* stage, f32x16 (&acc)[4], const flo
   __syncthreads();
 }
 
+// gbase rows += acc * mul (32 fp32 rows, row stride in elements), staged through LDS both ways
+// like load_rows_f32 / store_rows_f32.  Contains block-wide barriers: every wave must call it.
+__device__ inline void add_rows_f32(uint8_t* stage, const f32x16 (&acc)[4], const float mul, float* gbase,
+                                    int64_t row_stride, int rows_valid) {
+  f32x16 t[4];
+  load_rows_f32(stage, t, gbase, row_stride, rows_valid);
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) t[db][i] = __builtin_fmaf(acc[db][i], mul, t[db][i]);
+  store_rows_f32(stage, t, 1.f, gbase, row_stride, rows_valid);
+}
+
 // Pack 8 consecutive accumulator elements (u*8 .. u*8+7) into one bf16x8 MFMA operand.
 __device__ __forceinline__ bf16x8 pack8(const f32x16& s, int u) {
   u32x4 w;

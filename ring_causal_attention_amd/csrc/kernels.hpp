@@ -71,6 +71,12 @@ struct BwdParams {
   uint16_t* dk;
   uint16_t* dv;
   Strides sdq, sdk, sdv;
+  // backward ring step: when set, the gradients are added into these float32 tensors instead
+  // of being stored to dq / dk / dv
+  float* dq_acc;
+  float* dk_acc;
+  float* dv_acc;
+  Strides sdqa, sdka, sdva;
 };
 
 hipError_t launch_rope(const RopeParams& p, bool bf16, hipStream_t stream);

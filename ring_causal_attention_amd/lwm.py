@@ -35,7 +35,7 @@ class Tensor4(ctypes.Structure):
 
 _lib = None
 EXPORTS = ["lwm_abi_version", "lwm_last_error", "lwm_rope_apply", "lwm_blockattn_fwd",
-           "lwm_blockattn_bwd_workspace_size", "lwm_blockattn_bwd", "lwm_ring_step",
+           "lwm_blockattn_bwd_workspace_size", "lwm_blockattn_bwd", "lwm_ring_step", "lwm_ring_step_bwd",
            "lwm_profile_enable", "lwm_profile_reset", "lwm_profile_count", "lwm_profile_get"]
 
 
@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
     L.lwm_blockattn_bwd.argtypes = [P, P, P, P, VP, P, VP, VP, I64, I64, I32, F32, P, P, P, VP, ctypes.c_size_t, VP]
     L.lwm_ring_step.restype = ctypes.c_int
     L.lwm_ring_step.argtypes = [P, P, P, VP, VP, I64, I64, I32, F32, P, VP, P, VP]
+    L.lwm_ring_step_bwd.restype = ctypes.c_int
+    L.lwm_ring_step_bwd.argtypes = [P, P, P, P, VP, P, VP, VP, I64, I64, I32, F32, P, P, P, VP, ctypes.c_size_t, VP]
     L.lwm_profile_enable.restype = ctypes.c_int
     L.lwm_profile_enable.argtypes = [I32]
     L.lwm_profile_reset.restype = ctypes.c_int
@@ -172,6 +174,22 @@ def lwm_ring_step(q, k_shard, v_shard, o_acc, lse_acc, seg_q=None, seg_k=None, q
                                _ptr(_seg(seg_k)), int(q_offset), int(k_offset), int(bool(causal)), float(scale),
                                _ref(tensor4(o_acc)), _ptr(lse_acc), _ref(tensor4(o_final)), _stream(q)))
     return o_acc, lse_acc
+
+
+def lwm_ring_step_bwd(q, k_shard, v_shard, o, lse, dout, dq_acc, dk_acc, dv_acc, seg_q=None, seg_k=None,
+                      q_offset=0, k_offset=0, causal=True, scale=0.0, workspace=None):
+    """Add one KV shard's share of the gradients into dq_acc (float32, like q) and dk_acc,
+    dv_acc (float32, like k_shard), in place; o and lse are the forward's results over all shards."""
+    B, Lq, H, D = q.shape
+    need = lwm_blockattn_bwd_workspace_size(B, H, Lq, k_shard.shape[1], D)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(lib().lwm_ring_step_bwd(_ref(tensor4(q)), _ref(tensor4(k_shard)), _ref(tensor4(v_shard)), _ref(tensor4(o)),
+                                   _ptr(lse), _ref(tensor4(dout)), _ptr(_seg(seg_q)), _ptr(_seg(seg_k)), int(q_offset),
+                                   int(k_offset), int(bool(causal)), float(scale), _ref(tensor4(dq_acc)),
+                                   _ref(tensor4(dk_acc)), _ref(tensor4(dv_acc)), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(q)))
+    return dq_acc, dk_acc, dv_acc
 
 
 def lwm_profile_enable(on: bool = True):

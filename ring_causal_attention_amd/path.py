@@ -42,6 +42,39 @@ def ring_forward(q_rot, k_shards, v_shards, shard_order, shard_len, q_offset, ca
     return o_final, o_acc, lse_acc
 
 
+def ring_backward(q_rot, k_shards, v_shards, o, lse, dout, shard_order, shard_len, q_offset, causal=True,
+                  scale=0.0, seg_q=None, seg_k_shards=None, dq_acc=None, dk_acc=None, dv_acc=None, workspace=None):
+    """Backward ring for one query block: visit the KV shards in ``shard_order`` and add each
+    shard's share of the gradients into ``dq_acc`` (float32 [B, Lq, H, D]) and into the shard's
+    own ``dk_acc[j]``, ``dv_acc[j]`` (float32 [B, shard_len, H, D]; on a ring these travel with
+    the shard).  o and lse are the forward's results over all shards (``ring_forward``).  Shards
+    wholly in the causal future of the block are skipped: they add zero.  Accumulators that are
+    not given start at zero.  Returns (dq_acc, dk_acc, dv_acc), the last two dicts by shard.
+    """
+    B, Lq, H, D = q_rot.shape
+    dev = q_rot.device
+    if dq_acc is None:
+        dq_acc = torch.zeros((B, Lq, H, D), dtype=torch.float32, device=dev)
+    dk_acc = {} if dk_acc is None else dk_acc
+    dv_acc = {} if dv_acc is None else dv_acc
+    if workspace is None:
+        need = lwm.lwm_blockattn_bwd_workspace_size(B, H, Lq, shard_len, D)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    last_q = q_offset + Lq - 1
+    for j in shard_order:
+        if causal and j * shard_len > last_q:
+            continue
+        kj = k_shards[j]
+        if j not in dk_acc:
+            dk_acc[j] = torch.zeros(kj.shape, dtype=torch.float32, device=dev)
+        if j not in dv_acc:
+            dv_acc[j] = torch.zeros(kj.shape, dtype=torch.float32, device=dev)
+        lwm.lwm_ring_step_bwd(q_rot, kj, v_shards[j], o, lse, dout, dq_acc, dk_acc[j], dv_acc[j], seg_q=seg_q,
+                              seg_k=None if seg_k_shards is None else seg_k_shards[j], q_offset=q_offset,
+                              k_offset=j * shard_len, causal=causal, scale=scale, workspace=workspace)
+    return dq_acc, dk_acc, dv_acc
+
+
 def attention_forward(q, k, v, theta, seg=None, layout="half", causal=True, scale=0.0, q_offset=0, k_offset=0,
                       pos_q_offset=None, pos_k_offset=None):
     """RoPE(Q), RoPE(K), blockwise forward.  Positions restart per segment when ``seg`` is given."""

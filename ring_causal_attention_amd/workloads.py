@@ -18,13 +18,13 @@ def host_inputs(w: Workload, threads: int = 8) -> dict:
     out: dict = {"workload": w}
     if w.ring_shards:
         vis = list(range(w.ring_index + 1))
-        reqs = [(w.seed, "q", shape_q, None)]
+        reqs = [(w.seed, "q", shape_q, None), (w.seed, "do", shape_q, None)]
         reqs += [(w.seed, t, (w.B, w.Lq, w.H, w.D), j) for t in ("k", "v") for j in vis]
         arrs = synth.normal_many(reqs, threads)
-        out["q"] = arrs[0]
+        out["q"], out["do"] = arrs[0], arrs[1]  # dO: upstream gradient of the backward ring
         n = len(vis)
-        out["k_shards"] = dict(zip(vis, arrs[1:1 + n]))
-        out["v_shards"] = dict(zip(vis, arrs[1 + n:1 + 2 * n]))
+        out["k_shards"] = dict(zip(vis, arrs[2:2 + n]))
+        out["v_shards"] = dict(zip(vis, arrs[2 + n:2 + 2 * n]))
         out["seg"] = None
         return out
     names = ["q", "k", "v"] + (["do"] if w.backward else [])

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol():
     assert set(names) == set(lwm.EXPORTS), names
     for n in names:
         assert hasattr(L, n), n
-    assert L.lwm_abi_version() == 1
+    assert L.lwm_abi_version() == 2
     assert L.lwm_last_error() == b""
 
 
@@ -91,6 +91,26 @@ def test_backward_and_ring_validation():
     oacc = t4(dtype=1, L=9)
     st = L.lwm_ring_step(r(q), r(q), r(q), None, None, 0, 0, 1, 0.0, r(oacc), 16, None, None)
     assert st == -1
+
+
+def test_ring_backward_validation():
+    L = _lib()
+    r = ctypes.byref
+    q = t4()
+    acc = t4(dtype=1)
+    ws = L.lwm_blockattn_bwd_workspace_size(1, 2, 8, 8, 128)
+    args = lambda dqa, dka, dva, lse=16, nbytes=ws: (r(q), r(q), r(q), r(q), lse, r(q), None, None, 0, 0, 1, 0.0,
+                                                    r(dqa), r(dka), r(dva), 256, nbytes, None)
+    st = L.lwm_ring_step_bwd(*args(q, acc, acc))  # bf16 accumulator
+    assert st == -1 and "float32" in L.lwm_last_error().decode()
+    st = L.lwm_ring_step_bwd(*args(acc, t4(dtype=1, L=9), acc))
+    assert st == -1 and "mismatch" in L.lwm_last_error().decode()
+    st = L.lwm_ring_step_bwd(*args(acc, acc, acc, nbytes=ws - 1))
+    assert st == -3 and "workspace" in L.lwm_last_error().decode()
+    st = L.lwm_ring_step_bwd(*args(acc, acc, acc, lse=None))
+    assert st == -1 and "lse" in L.lwm_last_error().decode()
+    assert L.lwm_ring_step_bwd(r(q), r(q), r(q), r(q), 16, r(q), 16, None, 0, 0, 1, 0.0, r(acc), r(acc), r(acc),
+                               256, ws, None) == -1
 
 
 def test_rope_validation():

@@ -135,6 +135,47 @@ def test_ring_share_1M_sampled():
     check_rows(o, lse, ro, rl, rows, "bf16", heads=heads)
 
 
+def test_ring_share_1M_backward_sampled():
+    need_gpu()
+    w = W["ring_share_1M"]
+    note(f"workload {w.name} backward")
+    h = workloads.host_inputs(w)
+    d = workloads.device_inputs(h)
+    S, r = w.Lq, w.ring_index
+    qr = lwm.lwm_rope_apply(d["q"], pos_offset=w.q_offset, theta=w.theta)
+    kr = {j: lwm.lwm_rope_apply(x, pos_offset=j * S, theta=w.theta) for j, x in d["k_shards"].items()}
+    o, _, lse = path.ring_forward(qr, kr, d["v_shards"], w.ring_order(), S, w.q_offset)
+    dq_acc, dk_acc, dv_acc = path.ring_backward(qr, kr, d["v_shards"], o, lse, d["do"], w.ring_order(), S, w.q_offset)
+    torch.cuda.synchronize()
+    assert sorted(dk_acc) == list(range(r + 1))
+    # at any size: rows of P sum to one over all keys, so sum over every key of dV = sum_i dO_i
+    sdv = sum(x.sum(dim=1) for x in dv_acc.values()).cpu().numpy()
+    sdo = exact(h["do"], "bf16").sum(axis=1)
+    assert np.linalg.norm(sdv - sdo) <= 1e-2 * np.linalg.norm(sdo)
+    # sampled query rows of dQ (w.r.t. the rotated Q) against the oracle's ring steps summed
+    heads = [0, 5]
+    rows = sample_rows(S, n_random=3, seed=5)[::3]
+    k_all = np.concatenate([h["k_shards"][j] for j in range(r + 1)], axis=1)
+    v_all = np.concatenate([h["v_shards"][j] for j in range(r + 1)], axis=1)
+    pos_q = oracle.positions(w.B, S, w.q_offset)
+    pos_k = oracle.positions(w.B, k_all.shape[1])
+    ro, rl = oracle_rows(h["q"], k_all, v_all, rows, w.theta, "bf16", pos_q, pos_k, q_offset=w.q_offset,
+                         heads=heads)
+    kr_all = oracle.rope(exact(k_all[:, :, heads], "bf16"), pos_k, w.theta)
+    vr_all = exact(v_all[:, :, heads], "bf16")
+    ref = np.zeros((w.B, len(rows), len(heads), w.D))
+    for n, row in enumerate(rows):
+        qrow = oracle.rope(exact(h["q"][:, row:row + 1][:, :, heads], "bf16"), pos_q[:, row:row + 1], w.theta)
+        dorow = exact(h["do"][:, row:row + 1][:, :, heads], "bf16")
+        for j in range(r + 1):
+            sl = slice(j * S, (j + 1) * S)
+            dqj, _, _ = oracle.ring_step_bwd(qrow, kr_all[:, sl], vr_all[:, sl], ro[:, n:n + 1],
+                                             rl[:, :, n:n + 1], dorow, None, None, w.q_offset + row, j * S, True)
+            ref[:, n] += dqj[:, 0]
+    got = host(dq_acc[:, rows][:, :, heads])
+    assert rel_fro(got, ref) <= GRAD_REL_FRO, rel_fro(got, ref)
+
+
 def test_train_step_L32768_one_head():
     need_gpu()
     w = W["train_step_L32768"]
