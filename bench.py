@@ -166,7 +166,24 @@ def bench_extras(torch, lwm, path, workloads, configs, steps=3, warmup=1):
     out[w.name] = {"ms_per_step": ms, "attn_fwd_ms": fk, "attn_fwd_tflops": w.fwd_flop() / fk / 1e9,
                    "pct_of_bf16_peak": 100 * w.fwd_flop() / fk / 1e9 / configs.PEAK_BF16_TFLOPS,
                    "segments": len(w.segment_lengths()), "visible_pairs": w.visible_pairs(), "kernels": ks}
-    del d, qr, kr, o, lse
+    # the same packed row through a whole training step (forward + backward, segment-aware tile
+    # skipping in both backward kernels); dO drawn like the other tensors of the workload
+    from ring_causal_attention_amd import synth
+    do = workloads.to_device(synth.normal(w.seed, "do", (w.B, w.Lq, w.H, w.D)), w.dtype)
+    bufs = path.TrainStepBuffers(d["q"], d["k"])
+
+    def packed_train_step():
+        path.training_step(d["q"], d["k"], d["v"], do, w.theta, seg=d["seg"], buffers=bufs)
+
+    ms, prof = time_steps(packed_train_step, steps, warmup, lwm, torch)
+    ks = kernels_table(prof, steps)
+    tflop = 14 * w.D * w.visible_pairs()
+    bk = sum(ks[k]["ms_per_step"] for k in ("bwd_delta", "bwd_dq", "bwd_dkdv") if k in ks)
+    out[w.name + "_train"] = {"ms_per_step": ms, "tflops": tflop / ms / 1e9,
+                              "pct_of_bf16_peak": 100 * tflop / ms / 1e9 / configs.PEAK_BF16_TFLOPS,
+                              "attn_bwd_ms": bk, "attn_bwd_tflops": 10 * w.D * w.visible_pairs() / bk / 1e9,
+                              "tokens_per_s": w.B * w.Lq / (ms * 1e-3), "kernels": ks}
+    del d, qr, kr, o, lse, do, bufs
     torch.cuda.empty_cache()
 
     # one device's share of a 1M-token ring: 41 visible shards folded by lwm_ring_step

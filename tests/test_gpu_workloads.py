@@ -113,6 +113,44 @@ def test_packed_L65536_sampled():
     assert torch.equal(o[:, starts].float(), d["v"][:, starts].float())
 
 
+def test_packed_L65536_training_step_one_head():
+    need_gpu()
+    w = W["packed_L65536"]
+    note(f"workload {w.name} training step")
+    h = workloads.host_inputs(w)
+    from ring_causal_attention_amd import synth
+    do_h = synth.normal(w.seed, "do", (w.B, w.Lq, w.H, w.D))
+    d = workloads.device_inputs(h)
+    o, lse, dq, dk, dv = path.training_step(d["q"], d["k"], d["v"], workloads.to_device(do_h, w.dtype), w.theta,
+                                            seg=d["seg"])
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv):
+        assert not bool(torch.isnan(t).any())
+    # every row sees at least itself: sum over keys of dV = sum over queries of dO, all heads
+    sdv = dv.float().sum(dim=1).cpu().numpy()
+    sdo = exact(do_h, "bf16").sum(axis=1)
+    assert np.linalg.norm(sdv - sdo) <= 1e-2 * np.linalg.norm(sdo)
+    # one full head against the oracle, segment by segment: a packed segment is exactly an
+    # unpacked causal sequence of its own with positions from 0 (an oracle pin checks this)
+    hh = 11
+    sl = lambda x, a, b: exact(x[:, a:b, hh:hh + 1], "bf16")
+    ro, rdq, rdk, rdv = (np.zeros((w.B, w.Lq, 1, w.D)) for _ in range(4))
+    start = 0
+    for n in w.segment_lengths():
+        a, b = start, start + n
+        pos = oracle.positions(w.B, n)
+        o_s, _, dq_s, dk_s, dv_s = oracle.training_step(sl(h["q"], a, b), sl(h["k"], a, b), sl(h["v"], a, b),
+                                                        sl(do_h, a, b), pos, pos, w.theta, "half")
+        ro[:, a:b], rdq[:, a:b], rdk[:, a:b], rdv[:, a:b] = o_s, dq_s, dk_s, dv_s
+        start = b
+    assert start == w.Lq
+    mx, mean = errors(host(o[:, :, hh:hh + 1]), ro)
+    assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (mx, mean)
+    for name, g, ref in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+        e = rel_fro(host(g[:, :, hh:hh + 1]), ref)
+        assert e <= GRAD_REL_FRO, (name, e)
+
+
 def test_ring_share_1M_sampled():
     need_gpu()
     w = W["ring_share_1M"]
