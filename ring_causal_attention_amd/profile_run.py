@@ -1,5 +1,7 @@
 """Driver for rocprofv3 runs of the hot path, and the summariser of their counter output.
 
+``--ring-backward`` runs the backward ring of a ring workload (after one forward ring).
+
 Run under the profiler (one counter pass per run, e.g. ``--pmc FETCH_SIZE``):
 
     rocprofv3 --pmc FETCH_SIZE -d OUT -o fetch -- python3 -m ring_causal_attention_amd.profile_run \
@@ -25,12 +27,20 @@ from collections import defaultdict
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def run_workload(name: str, steps: int):
+def run_workload(name: str, steps: int, ring_backward: bool = False):
     import torch
     from . import configs, lwm, path, workloads
     w = configs.WORKLOADS[name]
     d = workloads.device_inputs(workloads.host_inputs(w))
-    if w.backward:
+    if ring_backward:
+        if not w.ring_shards:
+            raise SystemExit("--ring-backward needs a ring workload")
+        S = w.Lq
+        qr = lwm.lwm_rope_apply(d["q"], pos_offset=w.q_offset, theta=w.theta)
+        kr = {j: lwm.lwm_rope_apply(x, pos_offset=j * S, theta=w.theta) for j, x in d["k_shards"].items()}
+        o, _, lse = path.ring_forward(qr, kr, d["v_shards"], w.ring_order(), S, w.q_offset)
+        step = lambda: path.ring_backward(qr, kr, d["v_shards"], o, lse, d["do"], w.ring_order(), S, w.q_offset)
+    elif w.backward:
         bufs = path.TrainStepBuffers(d["q"], d["k"])
         step = lambda: path.training_step(d["q"], d["k"], d["v"], d["do"], w.theta, buffers=bufs)
     elif w.ring_shards:
@@ -103,6 +113,7 @@ def main():
     ap.add_argument("--copy-mib", type=int, default=0)
     ap.add_argument("--summarize", default=None)
     ap.add_argument("--write", action="store_true", help="write profiles/traffic_<workload>.json")
+    ap.add_argument("--ring-backward", action="store_true", help="ring workloads: run the backward ring")
     args = ap.parse_args()
     if args.summarize:
         res = summarize(args.summarize, args.workload, args.copy_mib or 1024)
@@ -114,7 +125,7 @@ def main():
     if args.copy_mib:
         run_copy(args.copy_mib)
     else:
-        run_workload(args.workload, args.steps)
+        run_workload(args.workload, args.steps, args.ring_backward)
 
 
 if __name__ == "__main__":
