@@ -20,7 +20,6 @@
 //  Tiles travel HBM -> LDS by buffer loads that write LDS directly (double-buffered).  Recomputing
 //  S and dP in both kernels costs two extra products over the five the method needs; in exchange
 //  no partial dQ is ever written to or reduced through memory.
-#include <type_traits>
 
 #include "attn_common.hpp"
 #include "profile.hpp"
