@@ -301,6 +301,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdParams p)
     if (j + 1 < ntiles) issue_v(j + 1);
     if (need_mask(j)) apply_mask(j, s_cur);
     SoftmaxState x;
+    // the half with the vector work runs at raised wave priority: when this SIMD's other wave is
+    // in its pure-MFMA half, the softmax instructions issue first and the MFMAs fill around them
+    __builtin_amdgcn_s_setprio(1);
     if constexpr (kNext) {
       // MFMA q of S_(j+1) (K fragments four MFMAs ahead), then softmax slice q of tile j
       const uint8_t* kt = sm.t.k[(j + 1) & 1];
@@ -324,6 +327,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdParams p)
       for (int q = 0; q < 16; ++q) softmax_slice(q, s_cur, x);
     }
     rescale(x.alpha);
+    __builtin_amdgcn_s_setprio(0);
     mma_pv(j);
     wait_vmcnt<0>();
     __syncthreads();
