@@ -32,7 +32,7 @@ def log(msg):
 
 
 def kernel_work(w, name):
-    """Algorithmic (flop, bytes) of one launch of `name` on workload w (see DESIGN.md)."""
+    """Algorithmic (flop, bytes) of one launch of `name` on workload w."""
     pairs, D = w.visible_pairs(), w.D
     t = w.tensor_bytes()
     lse_bytes = 4 * w.B * w.H * w.Lq
@@ -252,7 +252,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}, "
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus}, "
               f"WORLD_SIZE={world}).  The ring is simulated on one GPU as a loop over KV shards.", file=sys.stderr)
         sys.exit(2)
 
