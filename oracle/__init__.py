@@ -17,3 +17,4 @@ from .attention import (  # noqa: F401
     training_step,
     visible,
 )
+from .ffn import blockwise_ffn, silu, swiglu_ffn  # noqa: F401

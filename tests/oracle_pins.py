@@ -442,6 +442,57 @@ def pin_golden(orc):
         assert np.allclose(y[0, 0, 0], np.array(c["y"]), atol=1e-14, rtol=0), c["name"]
 
 
+# ---------------------------------------------------------------- feed-forward pins
+def _ffn_case(seed, M=13, d=12, f=20):
+    rng = _rng(seed, 7)
+    return (_rand(rng, M, d), _rand(rng, f, d) / math.sqrt(d), _rand(rng, f, d) / math.sqrt(d),
+            _rand(rng, d, f) / math.sqrt(f))
+
+
+def pin_ffn_brute_force(orc):
+    """Scalar loops with math.exp for z / (1 + e^-z)."""
+    x, wg, wu, wd = _ffn_case(30, M=5, d=6, f=7)
+    y, h = orc.swiglu_ffn(x, wg, wu, wd)
+    for m in range(5):
+        hh = []
+        for n in range(7):
+            g = math.fsum(x[m, k] * wg[n, k] for k in range(6))
+            u = math.fsum(x[m, k] * wu[n, k] for k in range(6))
+            hh.append(g / (1.0 + math.exp(-g)) * u)
+            assert abs(h[m, n] - hh[-1]) < 1e-13
+        for j in range(6):
+            assert abs(y[m, j] - math.fsum(hh[n] * wd[j, n] for n in range(7))) < 1e-12
+
+
+def pin_ffn_torch(orc):
+    """Library routine: torch.nn.functional.silu and matmul (CPU float64), the LLaMA block."""
+    import torch
+    import torch.nn.functional as F
+    x, wg, wu, wd = _ffn_case(31, M=40, d=32, f=88)
+    t = [torch.from_numpy(a) for a in (x, wg, wu, wd)]
+    ref = (F.silu(t[0] @ t[1].T) * (t[0] @ t[2].T)) @ t[3].T
+    assert np.allclose(orc.swiglu_ffn(x, wg, wu, wd)[0], ref.numpy(), atol=1e-12, rtol=0)
+
+
+def pin_silu_identities(orc):
+    z = np.concatenate([np.linspace(-40, 40, 801), [0.0, 1e-300, -1e-300, 700.0, -700.0]])
+    s = orc.silu(z)
+    assert np.allclose(s - orc.silu(-z), z, atol=1e-12, rtol=1e-15)   # z sig(z) + z sig(-z) = z
+    assert s[np.argmin(np.abs(z))] == 0.0 and np.isfinite(s).all()
+    assert abs(orc.silu(700.0) - 700.0) < 1e-9 and abs(orc.silu(-700.0)) < 1e-9
+    assert abs(orc.silu(1.0) - 1.0 / (1.0 + math.exp(-1.0))) < 1e-15
+
+
+def pin_ffn_blockwise_invariance(orc):
+    """Chunking the token axis (scan_mlp_chunk_size) leaves the result unchanged."""
+    x, wg, wu, wd = _ffn_case(32, M=29, d=16, f=24)
+    full = orc.swiglu_ffn(x, wg, wu, wd)[0]
+    for chunk in (1, 3, 7, 8, 29, 64):
+        assert np.allclose(orc.blockwise_ffn(x, wg, wu, wd, chunk), full, atol=1e-13, rtol=0), chunk
+
+
+FFN_PINS = [pin_ffn_brute_force, pin_ffn_torch, pin_silu_identities, pin_ffn_blockwise_invariance]
+
 ALL_PINS = [
     pin_forward_brute_force, pin_forward_sdpa, pin_forward_closed_forms, pin_forward_invariants,
     pin_packed_equals_unpacked, pin_block_and_ring_invariance, pin_rope, pin_segment_positions,

@@ -43,10 +43,24 @@ MUTANTS = [
 ]
 
 
-def mutant(old, new):
-    assert SRC.count(old) >= 1, f"mutation anchor vanished: {old!r}"
+FFN_SRC = open(os.path.join(ROOT, "oracle", "ffn.py"), encoding="utf-8").read()
+
+# the same for the feed-forward oracle (checked against its own pins)
+FFN_MUTANTS = [
+    ("ffn_gate_dropped", "h = silu(x @ np.asarray(w_gate, dtype=np.float64).T) * (x @", "h = 1.0 * (x @"),
+    ("ffn_gate_and_up_swapped", "h = silu(x @ np.asarray(w_gate, dtype=np.float64).T) * (x @ np.asarray(w_up,",
+     "h = silu(x @ np.asarray(w_up, dtype=np.float64).T) * (x @ np.asarray(w_gate,"),
+    ("silu_is_sigmoid", "    return z * sig", "    return sig"),
+    ("silu_negative_branch_wrong", "np.where(z >= 0, 1.0 / (1.0 + e), e / (1.0 + e))", "np.where(z >= 0, 1.0 / (1.0 + e), 1.0 / (1.0 + e))"),
+    ("ffn_down_not_transposed", "y = h @ np.asarray(w_down, dtype=np.float64).T", "y = h @ np.asarray(w_down, dtype=np.float64).T[::-1]"),
+    ("blockwise_last_chunk_dropped", "for r0 in range(0, M, max(1, int(chunk))):", "for r0 in range(0, M - 1, max(1, int(chunk))):"),
+]
+
+
+def mutant(old, new, src=SRC):
+    assert src.count(old) >= 1, f"mutation anchor vanished: {old!r}"
     mod = types.ModuleType("oracle_mutant")
-    exec(compile(SRC.replace(old, new, 1), "oracle_mutant", "exec"), mod.__dict__)
+    exec(compile(src.replace(old, new, 1), "oracle_mutant", "exec"), mod.__dict__)
     return mod
 
 
@@ -55,6 +69,18 @@ def test_planted_mistake_is_caught(name, old, new):
     mod = mutant(old, new)
     caught = []
     for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(mod)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught the planted mistake {name}"
+
+
+@pytest.mark.parametrize("name,old,new", FFN_MUTANTS, ids=[m[0] for m in FFN_MUTANTS])
+def test_planted_ffn_mistake_is_caught(name, old, new):
+    mod = mutant(old, new, FFN_SRC)
+    caught = []
+    for pin in oracle_pins.FFN_PINS:
         try:
             pin(mod)
         except AssertionError:
