@@ -9,8 +9,8 @@ causal-attention TFLOP/s of forward + backward (visible pairs only, 4*D + 10*D f
 
 Also reported: per-kernel durations from HIP events recorded around every launch on its
 stream during the timed steps, the roofline of the dominant kernel, the CPU oracle timed on a
-bounded sample of the same workload, and (unless --no-extras) the forward-only, packed and
-ring workloads as extra lines inside the same JSON object.
+bounded sample of the same workload, and (unless --no-extras) the forward-only, packed, ring
+and feed-forward workloads as extra lines inside the same JSON object.
 """
 from __future__ import annotations
 
@@ -237,6 +237,54 @@ def bench_extras(torch, lwm, path, workloads, configs, steps=3, warmup=1):
         "note": "10*D flop per visible pair; ms_per_step also zeroes the float32 accumulators",
         "kernels": ks}
     del d, qr, kr, o_acc, lse_acc, o, dq_acc, dk_acc, dv_acc, ws
+    torch.cuda.empty_cache()
+
+    # the blockwise feed-forward block that follows the attention (LLaMA-7B SwiGLU, chunks of
+    # 8192 rows), timed beside the same three products through torch.matmul (hipBLASLt)
+    fw = configs.FFN_WORKLOADS["ffn_llama7b_L32768"]
+    from ring_causal_attention_amd import synth
+    hf = synth.ffn_inputs(fw.seed, fw.rows, fw.d_model, fw.d_ff)
+    df = {k: workloads.to_device(v, "bf16") for k, v in hf.items()}
+    del hf
+    y = torch.empty_like(df["x"])
+    fws = torch.empty(lwm.lwm_blockwise_ffn_workspace_size(fw.rows, fw.d_ff, fw.chunk), dtype=torch.uint8,
+                      device="cuda")
+
+    def ffn_step():
+        lwm.lwm_blockwise_ffn(df["x"], df["w_gate"], df["w_up"], df["w_down"], chunk=fw.chunk, y=y, workspace=fws)
+
+    ms, prof = time_steps(ffn_step, steps, warmup, lwm, torch)
+    ks = kernels_table(prof, steps)
+    per_chunk = 2 * fw.chunk * fw.d_model * fw.d_ff
+    roof = {}
+    for name, mult in (("ffn_gate_up", 2), ("ffn_down", 1)):
+        if name in ks:
+            ach = mult * per_chunk / (ks[name]["avg_ms"] * 1e-3) / 1e12
+            roof[name] = {"bound": "mfma", "achieved": ach, "peak": configs.PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                          "frac": ach / configs.PEAK_BF16_TFLOPS, "avg_ms": ks[name]["avg_ms"]}
+    wg, wu, wd = df["w_gate"], df["w_up"], df["w_down"]
+
+    def torch_step():
+        for r0 in range(0, fw.rows, fw.chunk):
+            xc = df["x"][r0:r0 + fw.chunk]
+            torch.matmul(torch.nn.functional.silu(torch.matmul(xc, wg.t())) * torch.matmul(xc, wu.t()), wd.t(),
+                         out=y[r0:r0 + fw.chunk])
+
+    for _ in range(warmup):
+        torch_step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        torch_step()
+    torch.cuda.synchronize()
+    torch_ms = (time.perf_counter() - t0) * 1e3 / steps
+    out[fw.name] = {"ms_per_step": ms, "tflops": fw.flop() / ms / 1e9,
+                    "pct_of_bf16_peak": 100 * fw.flop() / ms / 1e9 / configs.PEAK_BF16_TFLOPS,
+                    "tokens_per_s": fw.rows / (ms * 1e-3), "roofline": roof,
+                    "torch_matmul_ms_per_step": torch_ms,
+                    "note": "6*rows*d_model*d_ff flop; torch_matmul_ms_per_step runs the same three products "
+                            "through torch.matmul and silu for comparison", "kernels": ks}
+    del df, y, fws
     torch.cuda.empty_cache()
     return out
 

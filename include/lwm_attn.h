@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define LWM_ABI_VERSION 2
+#define LWM_ABI_VERSION 3
 
 typedef enum {
   LWM_OK = 0,
@@ -181,6 +181,34 @@ int lwm_ring_step_bwd(const lwm_tensor4* q, const lwm_tensor4* k_shard, const lw
                       int64_t k_offset, int32_t causal, float scale, const lwm_tensor4* dq_acc,
                       const lwm_tensor4* dk_acc, const lwm_tensor4* dv_acc, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/*
+ * Blockwise feed-forward block: the transformer half that follows each attention, computed in
+ * chunks of rows along the sequence ("LWM：突破 100 万 Token 的开源大模型", section 配置参数,
+ * scan_mlp and scan_mlp_chunk_size; section 脚本运行说明 uses chunks of 8192).  The block is the
+ * LLaMA one the PyTorch port of the models loads (same page, section 运行 PyTorch 模型):
+ *     h = silu(x W_gate^T) * (x W_up^T),   y = h W_down^T,   silu(z) = z / (1 + e^-z),
+ * no biases.  Chunks are independent, so the result does not depend on `chunk` beyond rounding.
+ *
+ * All operands are bf16, row-major device matrices with leading dimensions in elements:
+ *   x       [rows, d_model]   leading dimension ldx  >= d_model
+ *   w_gate  [d_ff, d_model]   leading dimension ldw  >= d_model (nn.Linear layout [out, in])
+ *   w_up    [d_ff, d_model]   leading dimension ldw
+ *   w_down  [d_model, d_ff]   leading dimension ldwd >= d_ff
+ *   y       [rows, d_model]   leading dimension ldy  >= d_model (output; overlaps no input)
+ * Accumulation is float32; h is rounded to bf16 (it is the chunk's stored activation) and y is
+ * rounded to bf16 once.  d_model and d_ff must be multiples of 32; leading dimensions multiples
+ * of 8 and below 2^22; pointers 16-byte aligned.  `workspace` (caller-owned device memory, 256-
+ * byte aligned, at least lwm_blockwise_ffn_workspace_size bytes) holds one chunk's h.  rows = 0
+ * is a no-op.  Status: LWM_ERR_INVALID_ARG for NULL or misaligned pointers and bad sizes,
+ * LWM_ERR_UNSUPPORTED for sizes outside the ranges above, LWM_ERR_WORKSPACE for a short or
+ * misaligned workspace, LWM_ERR_HIP if a launch fails.
+ */
+size_t lwm_blockwise_ffn_workspace_size(int64_t rows, int64_t d_ff, int64_t chunk);
+int lwm_blockwise_ffn(const void* x, int64_t rows, int64_t d_model, int64_t ldx, const void* w_gate,
+                      const void* w_up, int64_t ldw, const void* w_down, int64_t ldwd, int64_t d_ff,
+                      void* y, int64_t ldy, int64_t chunk, void* workspace, size_t workspace_bytes,
+                      void* stream);
 
 /*
  * Kernel timing (instrumentation, not part of the method).  While enabled, every kernel the

@@ -105,6 +105,28 @@ WORKLOADS = {
     ]
 }
 
+@dataclasses.dataclass(frozen=True)
+class FfnWorkload:
+    """The blockwise feed-forward block after each attention layer: `rows` tokens through a
+    LLaMA-7B SwiGLU block (d_model 4096, d_ff 11008), `chunk` rows at a time."""
+    name: str
+    seed: int
+    rows: int
+    d_model: int
+    d_ff: int
+    chunk: int
+
+    def flop(self) -> int:
+        """Three products of rows x d_model x d_ff, 2 flop per multiply-add."""
+        return 6 * self.rows * self.d_model * self.d_ff
+
+
+FFN_WORKLOADS = {
+    w.name: w for w in [
+        FfnWorkload("ffn_llama7b_L32768", 1006, 32768, 4096, 11008, 8192),
+    ]
+}
+
 # MI355X (gfx950) published peaks used for roofline fractions.
 PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 4096 flop/clk x 2.4 GHz (AMD's "2.5 PFLOP/s" dense bf16)
 PEAK_FP32_MFMA_TFLOPS = 157.3

@@ -288,4 +288,52 @@ int lwm_ring_step(const lwm_tensor4* q, const lwm_tensor4* k_shard, const lwm_te
   return hip_status(lwm::launch_attn_fwd(p, true, static_cast<hipStream_t>(stream)), "ring step launch");
 }
 
+size_t lwm_blockwise_ffn_workspace_size(int64_t rows, int64_t d_ff, int64_t chunk) {
+  if (rows <= 0 || d_ff <= 0 || chunk <= 0) return 256;
+  const size_t bytes = (size_t)(chunk < rows ? chunk : rows) * (size_t)d_ff * 2;
+  return (bytes + 255) / 256 * 256;
+}
+
+int lwm_blockwise_ffn(const void* x, int64_t rows, int64_t d_model, int64_t ldx, const void* w_gate,
+                      const void* w_up, int64_t ldw, const void* w_down, int64_t ldwd, int64_t d_ff, void* y,
+                      int64_t ldy, int64_t chunk, void* workspace, size_t workspace_bytes, void* stream) {
+  if (rows < 0 || rows > (int64_t(1) << 31) - 1) return fail(LWM_ERR_INVALID_ARG, "rows must be in [0, 2^31)");
+  if (chunk < 1) return fail(LWM_ERR_INVALID_ARG, "chunk must be >= 1");
+  if (d_model <= 0 || d_ff <= 0 || d_model % 32 || d_ff % 32)
+    return fail(LWM_ERR_UNSUPPORTED, "d_model and d_ff must be positive multiples of 32 (got %lld, %lld)",
+                (long long)d_model, (long long)d_ff);
+  const struct {
+    const char* name;
+    int64_t ld, min;
+  } lds[] = {{"ldx", ldx, d_model}, {"ldw", ldw, d_model}, {"ldwd", ldwd, d_ff}, {"ldy", ldy, d_model}};
+  for (const auto& l : lds) {
+    if (l.ld < l.min) return fail(LWM_ERR_INVALID_ARG, "%s = %lld is below the row length %lld", l.name, (long long)l.ld, (long long)l.min);
+    if (l.ld % 8) return fail(LWM_ERR_INVALID_ARG, "%s must be a multiple of 8 elements (16 bytes)", l.name);
+    if (l.ld >= (int64_t(1) << 22))
+      return fail(LWM_ERR_UNSUPPORTED, "%s: rows of 8 MiB or more (tiles use 32-bit offsets)", l.name);
+  }
+  if (rows == 0) return ok();
+  const struct {
+    const char* name;
+    const void* p;
+  } ptrs[] = {{"x", x}, {"w_gate", w_gate}, {"w_up", w_up}, {"w_down", w_down}, {"y", y}};
+  for (const auto& q : ptrs) {
+    if (!q.p) return fail(LWM_ERR_INVALID_ARG, "%s is NULL", q.name);
+    if (reinterpret_cast<uintptr_t>(q.p) % 16) return fail(LWM_ERR_INVALID_ARG, "%s not 16-byte aligned", q.name);
+  }
+  const size_t need = lwm_blockwise_ffn_workspace_size(rows, d_ff, chunk);
+  if (!workspace || workspace_bytes < need)
+    return fail(LWM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(LWM_ERR_WORKSPACE, "workspace not 256-byte aligned");
+  lwm::FfnParams p{};
+  p.x = static_cast<const uint16_t*>(x); p.ldx = ldx;
+  p.w_gate = static_cast<const uint16_t*>(w_gate); p.w_up = static_cast<const uint16_t*>(w_up); p.ldw = ldw;
+  p.w_down = static_cast<const uint16_t*>(w_down); p.ldwd = ldwd;
+  p.y = static_cast<uint16_t*>(y); p.ldy = ldy;
+  p.h = static_cast<uint16_t*>(workspace);
+  p.rows = rows; p.chunk = chunk < rows ? chunk : rows;
+  p.d_model = (int)d_model; p.d_ff = (int)d_ff;
+  return hip_status(lwm::launch_ffn(p, static_cast<hipStream_t>(stream)), "feed-forward launch");
+}
+
 }  // extern "C"

@@ -79,8 +79,27 @@ struct BwdParams {
   Strides sdqa, sdka, sdva;
 };
 
+// Blockwise feed-forward block (bf16): y = (silu(x W_gate^T) * (x W_up^T)) W_down^T over chunks
+// of `chunk` rows; h is the [chunk, d_ff] workspace (leading dimension d_ff).  Leading
+// dimensions are in elements.
+struct FfnParams {
+  const uint16_t* x;
+  int64_t ldx;
+  const uint16_t* w_gate;
+  const uint16_t* w_up;
+  int64_t ldw;
+  const uint16_t* w_down;
+  int64_t ldwd;
+  uint16_t* y;
+  int64_t ldy;
+  uint16_t* h;
+  int64_t rows, chunk;
+  int d_model, d_ff;
+};
+
 hipError_t launch_rope(const RopeParams& p, bool bf16, hipStream_t stream);
 hipError_t launch_attn_fwd(const FwdParams& p, bool bf16, hipStream_t stream);
 hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t stream);
+hipError_t launch_ffn(const FfnParams& p, hipStream_t stream);
 
 }  // namespace lwm

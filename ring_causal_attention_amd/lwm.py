@@ -36,7 +36,7 @@ class Tensor4(ctypes.Structure):
 _lib = None
 EXPORTS = ["lwm_abi_version", "lwm_last_error", "lwm_rope_apply", "lwm_blockattn_fwd",
            "lwm_blockattn_bwd_workspace_size", "lwm_blockattn_bwd", "lwm_ring_step", "lwm_ring_step_bwd",
-           "lwm_profile_enable", "lwm_profile_reset", "lwm_profile_count", "lwm_profile_get"]
+           "lwm_blockwise_ffn_workspace_size", "lwm_blockwise_ffn", "lwm_profile_enable", "lwm_profile_reset", "lwm_profile_count", "lwm_profile_get"]
 
 
 def lib() -> ctypes.CDLL:
@@ -65,6 +65,10 @@ def lib() -> ctypes.CDLL:
     L.lwm_ring_step.argtypes = [P, P, P, VP, VP, I64, I64, I32, F32, P, VP, P, VP]
     L.lwm_ring_step_bwd.restype = ctypes.c_int
     L.lwm_ring_step_bwd.argtypes = [P, P, P, P, VP, P, VP, VP, I64, I64, I32, F32, P, P, P, VP, ctypes.c_size_t, VP]
+    L.lwm_blockwise_ffn_workspace_size.restype = ctypes.c_size_t
+    L.lwm_blockwise_ffn_workspace_size.argtypes = [I64, I64, I64]
+    L.lwm_blockwise_ffn.restype = ctypes.c_int
+    L.lwm_blockwise_ffn.argtypes = [VP, I64, I64, I64, VP, VP, I64, VP, I64, I64, VP, I64, I64, VP, ctypes.c_size_t, VP]
     L.lwm_profile_enable.restype = ctypes.c_int
     L.lwm_profile_enable.argtypes = [I32]
     L.lwm_profile_reset.restype = ctypes.c_int
@@ -190,6 +194,37 @@ def lwm_ring_step_bwd(q, k_shard, v_shard, o, lse, dout, dq_acc, dk_acc, dv_acc,
                                    _ref(tensor4(dk_acc)), _ref(tensor4(dv_acc)), _ptr(workspace),
                                    workspace.numel() * workspace.element_size(), _stream(q)))
     return dq_acc, dk_acc, dv_acc
+
+
+def _matrix(t, name):
+    if t.dtype != torch.bfloat16 or t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name}: expected a bf16 matrix with contiguous rows, got {t.dtype} {tuple(t.shape)}")
+    return t.stride(0) if t.shape[0] > 1 else t.shape[1]
+
+
+def lwm_blockwise_ffn_workspace_size(rows, d_ff, chunk) -> int:
+    return int(lib().lwm_blockwise_ffn_workspace_size(rows, d_ff, chunk))
+
+
+def lwm_blockwise_ffn(x, w_gate, w_up, w_down, chunk=8192, y=None, workspace=None):
+    """y = (silu(x W_gate^T) * (x W_up^T)) W_down^T over chunks of `chunk` rows; x [rows, d_model],
+    w_gate / w_up [d_ff, d_model], w_down [d_model, d_ff] (nn.Linear layout).  Returns y."""
+    rows, d_model = x.shape
+    d_ff = w_gate.shape[0]
+    if tuple(w_gate.shape) != (d_ff, d_model) or tuple(w_up.shape) != (d_ff, d_model) \
+            or tuple(w_down.shape) != (d_model, d_ff):
+        raise ValueError("weight shapes do not match x")
+    if w_gate.stride(0) != w_up.stride(0):
+        raise ValueError("w_gate and w_up must share a row stride")
+    y = torch.empty((rows, d_model), dtype=x.dtype, device=x.device) if y is None else y
+    if workspace is None:
+        workspace = torch.empty(lwm_blockwise_ffn_workspace_size(rows, d_ff, chunk), dtype=torch.uint8,
+                                device=x.device)
+    _check(lib().lwm_blockwise_ffn(_ptr(x), rows, d_model, _matrix(x, "x"), _ptr(w_gate), _ptr(w_up),
+                                   _matrix(w_gate, "w_gate"), _ptr(w_down), _matrix(w_down, "w_down"), d_ff, _ptr(y),
+                                   _matrix(y, "y"), int(chunk), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(x)))
+    return y
 
 
 def lwm_profile_enable(on: bool = True):

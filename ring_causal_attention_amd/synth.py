@@ -12,6 +12,9 @@ Recipe (every tensor is its own counter-addressed numpy stream):
   N(0, 1), the distribution the workloads name; for bf16 workloads the float32 draw is
   rounded to bfloat16 with round-to-nearest-even (``to_bf16_bits``) and both sides see
   the identical bf16 values;
+* feed-forward inputs (tensor ids x=5, W_gate=6, W_up=7, W_down=8): x is N(0, 1) (the block
+  sees RMS-normalised activations), weights are N(0, 1) draws times ``w_std`` = 0.02 (the usual
+  LLaMA initialisation scale; the pages give none), every array rounded to bfloat16;
 * segments (masked sequence packing, "LWM：突破 100 万 Token 的开源大模型" §概述 item (b), and
   the packing bullet of "[论文解读] World Model on Million-Length Video And Language With
   Blockwise RingAttention" §提出的方法): integer lengths drawn uniformly from an inclusive
@@ -22,7 +25,7 @@ from __future__ import annotations
 
 import numpy as np
 
-TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "do": 3, "seg": 4}
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "do": 3, "seg": 4, "x": 5, "w_gate": 6, "w_up": 7, "w_down": 8}
 
 
 def normal(seed: int, tensor: str, shape, shard: int | None = None) -> np.ndarray:
@@ -59,6 +62,19 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
     """float32 values that are exactly representable in bfloat16 (RNE of the input)."""
     return bf16_bits_to_f32(to_bf16_bits(x))
+
+
+def ffn_inputs(seed: int, rows: int, d_model: int, d_ff: int, w_std: float = 0.02, threads: int = 8) -> dict:
+    """float32 arrays holding bf16-representable values: x [rows, d_model], w_gate and w_up
+    [d_ff, d_model], w_down [d_model, d_ff]."""
+    reqs = [(seed, "x", (rows, d_model), None), (seed, "w_gate", (d_ff, d_model), None),
+            (seed, "w_up", (d_ff, d_model), None), (seed, "w_down", (d_model, d_ff), None)]
+    arrs = normal_many(reqs, threads)
+    out = {"x": round_to_bf16(arrs[0])}
+    for name, a in zip(("w_gate", "w_up", "w_down"), arrs[1:]):
+        a *= np.float32(w_std)
+        out[name] = round_to_bf16(a)
+    return out
 
 
 def segment_lengths(seed: int, total: int, lo: int, hi: int) -> list[int]:

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol():
     assert set(names) == set(lwm.EXPORTS), names
     for n in names:
         assert hasattr(L, n), n
-    assert L.lwm_abi_version() == 2
+    assert L.lwm_abi_version() == 3
     assert L.lwm_last_error() == b""
 
 
@@ -123,3 +123,34 @@ def test_rope_validation():
                          ((r(t4(D=24)), r(t4(D=24)), None, None, 0, 1e4, 0, 0, None), -2),
                          ((r(x), r(x), None, None, 0, 1e4, 0, 3, None), -1)]:
         assert L.lwm_rope_apply(*args) == status, args
+
+
+def test_ffn_validation():
+    L = _lib()
+    ws = L.lwm_blockwise_ffn_workspace_size(300, 96, 128)
+    assert ws >= 128 * 96 * 2 and ws % 256 == 0
+    assert L.lwm_blockwise_ffn_workspace_size(100, 96, 128) >= 100 * 96 * 2
+
+    def call(rows=300, d_model=64, ldx=64, x=256, wg=256, wu=256, ldw=64, wd=256, ldwd=96, d_ff=96, y=256, ldy=64,
+             chunk=128, ws_ptr=256, nbytes=ws):
+        st = L.lwm_blockwise_ffn(x, rows, d_model, ldx, wg, wu, ldw, wd, ldwd, d_ff, y, ldy, chunk, ws_ptr, nbytes,
+                                 None)
+        return st, L.lwm_last_error().decode()
+
+    for kwargs, status, needle in [
+        ({"x": None}, -1, "NULL"),
+        ({"wu": 264}, -1, "aligned"),
+        ({"d_model": 48, "ldx": 48, "ldw": 48, "ldy": 48}, -2, "multiples of 32"),
+        ({"d_ff": 0}, -2, "multiples of 32"),
+        ({"ldx": 32}, -1, "below"),
+        ({"ldwd": 100}, -1, "multiple of 8"),
+        ({"ldy": 1 << 22}, -2, "8 MiB"),
+        ({"chunk": 0}, -1, "chunk"),
+        ({"rows": -1}, -1, "rows"),
+        ({"nbytes": ws - 1}, -3, "workspace"),
+        ({"ws_ptr": 128}, -3, "aligned"),
+    ]:
+        st, msg = call(**kwargs)
+        assert st == status and needle in msg, (kwargs, st, msg)
+    # rows = 0 is a no-op that touches no pointer
+    assert call(rows=0, x=None, wg=None, wu=None, wd=None, y=None, ws_ptr=None, nbytes=0)[0] == 0
