@@ -27,9 +27,22 @@ from collections import defaultdict
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
+def run_ffn(name: str, steps: int):
+    import torch
+    from . import configs, lwm, synth, workloads
+    w = configs.FFN_WORKLOADS[name]
+    d = {k: workloads.to_device(v, "bf16") for k, v in synth.ffn_inputs(w.seed, w.rows, w.d_model, w.d_ff).items()}
+    for i in range(steps):
+        lwm.lwm_blockwise_ffn(d["x"], d["w_gate"], d["w_up"], d["w_down"], chunk=w.chunk)
+        torch.cuda.synchronize()
+        print(f"[profile_run] {name} step {i + 1}/{steps} done", flush=True)
+
+
 def run_workload(name: str, steps: int, ring_backward: bool = False):
     import torch
     from . import configs, lwm, path, workloads
+    if name in configs.FFN_WORKLOADS:
+        return run_ffn(name, steps)
     w = configs.WORKLOADS[name]
     d = workloads.device_inputs(workloads.host_inputs(w))
     if ring_backward:
@@ -71,6 +84,8 @@ def _short(kernel_name: str) -> str:
     for key in ("bwd_dkdv", "bwd_dq", "bwd_delta", "attn_fwd_bf16", "attn_fwd_f32", "rope_kernel"):
         if key in kernel_name:
             return key
+    if "ffn_gemm_kernel" in kernel_name:
+        return "ffn_gate_up" if "ILb1E" in kernel_name or "<true" in kernel_name else "ffn_down"
     return kernel_name.split("(")[0][-60:]
 
 
