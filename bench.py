@@ -97,7 +97,7 @@ def load_traffic(w):
     with open(p) as f:
         rec = json.load(f)
     from ring_causal_attention_amd import build
-    if rec.get("sources_sha") != build.sources_digest():
+    if rec.get("sources_sha") != build.sources_digest(rec.get("sources_family")):
         return None  # kernels changed since the counters were taken
     return {k: v["bytes_per_launch"] for k, v in rec.get("kernels", {}).items()}
 
@@ -256,12 +256,14 @@ def bench_extras(torch, lwm, path, workloads, configs, steps=3, warmup=1):
     ms, prof = time_steps(ffn_step, steps, warmup, lwm, torch)
     ks = kernels_table(prof, steps)
     per_chunk = 2 * fw.chunk * fw.d_model * fw.d_ff
+    traffic = load_traffic(fw) or {}
     roof = {}
     for name, mult in (("ffn_gate_up", 2), ("ffn_down", 1)):
         if name in ks:
             ach = mult * per_chunk / (ks[name]["avg_ms"] * 1e-3) / 1e12
             roof[name] = {"bound": "mfma", "achieved": ach, "peak": configs.PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                          "frac": ach / configs.PEAK_BF16_TFLOPS, "avg_ms": ks[name]["avg_ms"]}
+                          "frac": ach / configs.PEAK_BF16_TFLOPS, "traffic": traffic.get(name),
+                          "avg_ms": ks[name]["avg_ms"]}
     wg, wu, wd = df["w_gate"], df["w_up"], df["w_down"]
 
     def torch_step():

@@ -73,14 +73,21 @@ if __name__ == "__main__":
     build(save_temps="--save-temps" in sys.argv)
 
 
-def sources_digest() -> str:
-    """sha256 over the kernel sources and headers (identifies the code a measurement was taken on)."""
+# Kernel sources per family of kernels: a counter record taken on one family stays valid while
+# only another family's sources change.
+KERNEL_FAMILIES = {"attention": ["rope.hip", "attn_fwd.hip", "attn_bwd.hip"], "ffn": ["ffn.hip"]}
+
+
+def sources_digest(family: str | None = None) -> str:
+    """sha256 over the device headers and the kernel sources of `family` (all kernels when None):
+    identifies the code a measurement was taken on."""
     import hashlib
     hsh = hashlib.sha256()
-    names = sorted(n for n in os.listdir(CSRC) if n.endswith((".hip", ".hpp", ".cpp")))
+    hip = sorted(n for n in os.listdir(CSRC) if n.endswith(".hip"))
+    if family is not None:
+        hip = [n for n in hip if n in KERNEL_FAMILIES[family]]
+    names = sorted(n for n in os.listdir(CSRC) if n.endswith(".hpp")) + hip
     for n in names:
         with open(os.path.join(CSRC, n), "rb") as f:
             hsh.update(n.encode() + b"\0" + f.read())
-    with open(os.path.join(ROOT, "include", "lwm_attn.h"), "rb") as f:
-        hsh.update(f.read())
     return hsh.hexdigest()

@@ -117,7 +117,9 @@ def summarize(directory: str, workload: str, copy_mib: int):
                 kern[k] = {"read_bytes": rb, "write_bytes": wb, "bytes_per_launch": (rb or 0) + (wb or 0)}
         out["kernels"] = kern
     from .build import sources_digest
-    out["sources_sha"] = sources_digest()
+    from .configs import FFN_WORKLOADS
+    out["sources_family"] = "ffn" if workload in FFN_WORKLOADS else "attention"
+    out["sources_sha"] = sources_digest(out["sources_family"])
     return out
 
 
