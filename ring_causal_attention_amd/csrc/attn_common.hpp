@@ -86,6 +86,23 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Block-wide barrier that waits for nothing by itself: each wave first waits for exactly the
+// loads and LDS reads it must see finished (__syncthreads also drains every load still in
+// flight, including those of tiles further ahead).  The memory clobber keeps LDS accesses on
+// their side of it.
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// Wait until this wave's LDS reads (and other LGKM operations) have completed.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// Wait until at most n (0, 1 or 2) later groups of L vector-memory operations are in flight.
+template <int L>
+__device__ __forceinline__ void wait_groups(int n) {
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<L>(); break;
+    default: wait_vmcnt<2 * L>(); break;
+  }
+}
+
 // MFMA A operand "X^T" (32 features x 16 rows of X) read from a row-major swizzled tile with two
 // transposing reads.  Lane l receives feature db*32 + l%32 of rows g*16 + 4*(l/32) + {0..3} and
 // g*16 + 8 + 4*(l/32) + {0..3}: the row order of a 32x32 accumulator's lane half, so the B operand

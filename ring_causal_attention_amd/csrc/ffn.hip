@@ -37,20 +37,6 @@ __device__ __forceinline__ int swz4(int r) { return (r >> 2) & 3; }
 // byte offset of 16-byte chunk c of row r in a slab
 __device__ __forceinline__ int slab_off(int r, int c) { return r * kRowBytes + ((c ^ swz4(r)) << 4); }
 
-// Block-wide barrier that waits for nothing by itself: each wave first waits for exactly the
-// loads and LDS reads it must see finished (a plain __syncthreads would also drain the loads of
-// later slabs still in flight).  The memory clobber keeps LDS accesses on their side of it.
-__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }  // lgkmcnt(0) only
-template <int L>
-__device__ __forceinline__ void wait_slabs(int n_after) {  // at most n_after slabs of L loads outstanding
-  switch (n_after) {
-    case 0: wait_vmcnt<0>(); break;
-    case 1: wait_vmcnt<L>(); break;
-    default: wait_vmcnt<2 * L>(); break;
-  }
-}
-
 // Grid position -> (row tile, column tile).  When the grid is a multiple of 8, XCD x (the block
 // ids congruent to x mod 8) gets a contiguous range of the logical order; the logical order walks
 // groups of 8 row tiles column by column.
@@ -194,7 +180,7 @@ __global__ __launch_bounds__(kFfnWaves * kWave, kOcc) void ffn_gemm_kernel(const
 #pragma unroll
   for (int t = 0; t < kStages; ++t)
     if (t < nk) issue(t);
-  wait_slabs<kLoads>(min(nk - 1, kStages - 1));
+  wait_groups<kLoads>(min(nk - 1, kStages - 1));
   block_barrier();
   Frag f0, f1;
   read(0, 0, f0);
@@ -202,7 +188,7 @@ __global__ __launch_bounds__(kFfnWaves * kWave, kOcc) void ffn_gemm_kernel(const
   // next slab and, while slabs remain, loading slab t + kStages into the stage slab t used)
   auto slab = [&](auto kLoad, int t) {
     mma_interleaved(std::false_type{}, f0, 0, t, 1, f1);
-    wait_slabs<kLoads>(min(nk - 1, t + kStages - 1) - (t + 1));  // slab t + 1 has landed
+    wait_groups<kLoads>(min(nk - 1, t + kStages - 1) - (t + 1));  // slab t + 1 has landed
     wait_lgkm0();                                                // this wave's reads of slab t are done
     block_barrier();
     mma_interleaved(kLoad, f1, t + kStages, t + 1, 0, f0);
