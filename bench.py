@@ -39,6 +39,8 @@ def kernel_work(w, name):
     table = {
         "attn_fwd_bf16": (4 * D * pairs, w.fwd_bytes()),
         "attn_fwd_f32": (4 * D * pairs, w.fwd_bytes()),
+        # fused RoPE: reads pre-RoPE Q, also writes the rotated Q
+        "attn_fwd_rope_bf16": (4 * D * pairs, w.fwd_bytes() + t),
         # the dK/dV kernel forms S, dP, dV and dK: four of the backward's five products
         "bwd_dkdv": (8 * D * pairs, 6 * t),
         # the dQ kernel's share of the method's products is dQ (its S and dP are recomputation)
@@ -352,6 +354,20 @@ def main():
         "kernels": kernels,
         "roofline": roofline_for(w, kernels, configs, load_traffic(w)),
     }
+    # the same step with RoPE inside the attention calls (lwm_blockattn_fwd_rope / _bwd_rope):
+    # no RoPE pass over Q, no inverse-RoPE passes over dQ and dK
+    def fused_step():
+        path.training_step_fused(d["q"], d["k"], d["v"], d["do"], w.theta, buffers=bufs)
+
+    log("[bench] timing the fused-RoPE training step")
+    fms, fprof = time_steps(fused_step, args.steps, args.warmup, lwm, torch)
+    fks = kernels_table(fprof, args.steps)
+    result["train_step_rope_fused"] = {
+        "ms_per_step": fms, "tflops": flop / (fms * 1e-3) / 1e12,
+        "pct_of_bf16_peak": 100 * flop / (fms * 1e-3) / 1e12 / configs.PEAK_BF16_TFLOPS,
+        "tokens_per_s": w.B * w.Lq / (fms * 1e-3),
+        "note": "same workload and flop count as the headline step; dQ and dK rounded to bf16 once",
+        "kernels": fks}
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(w, h, w.theta, heads=args.cpu_heads)

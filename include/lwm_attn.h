@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define LWM_ABI_VERSION 3
+#define LWM_ABI_VERSION 4
 
 typedef enum {
   LWM_OK = 0,
@@ -93,7 +93,8 @@ const char* lwm_last_error(void);
  *     p = pos_offset + (pos ? pos[b*L + t] : seg ? t - first(b, t) : t)
  * where first(b, t) is the index of the first token of t's segment (positions restart at
  * each packed segment).  inv_freq_i = theta^(-2i/D); the angle p * inv_freq_i is formed and
- * reduced modulo 2*pi in double precision, its sine and cosine taken in single precision.
+ * reduced in double precision to r = angle - k*pi/2 (|r| <= pi/4), whose sine and cosine are summed
+ * from their Taylor series in double precision and rounded once to single precision.
  * Each pair (x_a, x_b) (layout selects the pairing) becomes
  *     (x_a cos - x_b sin,  x_a sin + x_b cos)       (inverse != 0: rotate by -angle).
  * x, y: same dtype (bf16: result rounded to nearest even; fp32) and shape [B, L, H, D] with
@@ -181,6 +182,56 @@ int lwm_ring_step_bwd(const lwm_tensor4* q, const lwm_tensor4* k_shard, const lw
                       int64_t k_offset, int32_t causal, float scale, const lwm_tensor4* dq_acc,
                       const lwm_tensor4* dk_acc, const lwm_tensor4* dv_acc, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/*
+ * RoPE inside the attention kernels (the two entry points below).  RoPE with theta scaled to
+ * the context length is the same operation as lwm_rope_apply ("[论文解读] World Model on
+ * Million-Length Video And Language With Blockwise RingAttention", section 提出的方法); the
+ * position of query row t is q_pos_offset + t and of key row t is k_pos_offset + t, or, when
+ * restart is 1, that offset plus t minus the first index of t's segment in seg_q (seg_k):
+ * positions restart at each packed segment ("LWM：突破 100 万 Token 的开源大模型", section 概述,
+ * item (b)).  restart = 1 needs segment ids.  theta > 0 and finite; |offsets| <= 2^40.
+ */
+typedef struct lwm_rope_args {
+  double theta;
+  int32_t layout;  /* lwm_rope_layout */
+  int32_t restart; /* 0 or 1 */
+  int64_t q_pos_offset;
+  int64_t k_pos_offset;
+} lwm_rope_args;
+
+/*
+ * Forward with RoPE applied inside the call (bf16 only): q and k are the pre-RoPE operands.
+ * Computes exactly what lwm_rope_apply on q (offset q_pos_offset, seg = restart ? seg_q : NULL),
+ * lwm_rope_apply on k (likewise), then lwm_blockattn_fwd on the rotated pair compute, bit for bit.
+ * The queries are rotated by each workgroup as it loads them into registers; the keys, which
+ * every query tile streams again, are rotated once by a pass into k_rot.
+ * k_rot: required bf16 output like k (the rotated keys; it may be k itself, with equal strides,
+ * for an in-place rotation).  q_rot: NULL or a bf16 output like q that receives the rotated
+ * queries (what lwm_blockattn_bwd_rope takes).  Other arguments and errors as for
+ * lwm_blockattn_fwd; rope may not be NULL.  Outputs overlap no input (except k_rot == k).
+ */
+int lwm_blockattn_fwd_rope(const lwm_tensor4* q, const lwm_tensor4* k, const lwm_tensor4* v,
+                           const int32_t* seg_q, const int32_t* seg_k, int64_t q_offset,
+                           int64_t k_offset, int32_t causal, float scale, const lwm_rope_args* rope,
+                           const lwm_tensor4* o, float* lse, const lwm_tensor4* q_rot,
+                           const lwm_tensor4* k_rot, void* stream);
+
+/*
+ * Backward with the inverse RoPE applied inside the call (bf16 only): q_rot and k_rot are the
+ * rotated operands the forward used (lwm_blockattn_fwd_rope's q_rot and k_rot); dq and dk are
+ * the gradients w.r.t. the pre-RoPE Q and K.  The result is lwm_blockattn_bwd's followed by
+ * lwm_rope_apply(inverse = 1) on dq and dk, except that dQ' and dK' are rotated back in float32
+ * inside the kernels and rounded to bf16 once (the separate route rounds twice).  dv is
+ * lwm_blockattn_bwd's bit for bit.  Arguments, workspace and errors as for lwm_blockattn_bwd;
+ * rope (as given to the forward) may not be NULL.
+ */
+int lwm_blockattn_bwd_rope(const lwm_tensor4* q_rot, const lwm_tensor4* k_rot, const lwm_tensor4* v,
+                           const lwm_tensor4* o, const float* lse, const lwm_tensor4* dout,
+                           const int32_t* seg_q, const int32_t* seg_k, int64_t q_offset,
+                           int64_t k_offset, int32_t causal, float scale, const lwm_rope_args* rope,
+                           const lwm_tensor4* dq, const lwm_tensor4* dk, const lwm_tensor4* dv,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Blockwise feed-forward block: the transformer half that follows each attention, computed in

@@ -89,6 +89,28 @@ int check_attention(const lwm_tensor4* q, const lwm_tensor4* k, const lwm_tensor
   return LWM_OK;
 }
 
+// Validates the fused-RoPE arguments and fills the kernels' copy (D = 128: 64 frequencies,
+// computed exactly as lwm_rope_apply computes them).
+int check_rope(const lwm_rope_args* r, bool have_segs, lwm::RopeFuse* out) {
+  if (!r) return fail(LWM_ERR_INVALID_ARG, "rope is NULL");
+  if (!(r->theta > 0.0) || !std::isfinite(r->theta)) return fail(LWM_ERR_INVALID_ARG, "theta must be finite and > 0");
+  if (r->layout != LWM_ROPE_HALF && r->layout != LWM_ROPE_INTERLEAVED)
+    return fail(LWM_ERR_INVALID_ARG, "unknown RoPE layout %d", r->layout);
+  if (r->restart != 0 && r->restart != 1) return fail(LWM_ERR_INVALID_ARG, "restart must be 0 or 1");
+  if (r->restart && !have_segs) return fail(LWM_ERR_INVALID_ARG, "restart = 1 needs seg_q and seg_k");
+  const int64_t lim = int64_t(1) << 40;
+  if (r->q_pos_offset < -lim || r->q_pos_offset > lim || r->k_pos_offset < -lim || r->k_pos_offset > lim)
+    return fail(LWM_ERR_INVALID_ARG, "position offsets must be in [-2^40, 2^40]");
+  *out = lwm::RopeFuse{};
+  out->on = 1;
+  out->layout = r->layout;
+  out->restart = r->restart;
+  out->q_pos_offset = r->q_pos_offset;
+  out->k_pos_offset = r->k_pos_offset;
+  for (int i = 0; i < lwm::kHeadDim / 2; ++i) out->inv_freq[i] = std::pow(r->theta, -2.0 * i / (double)lwm::kHeadDim);
+  return LWM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -148,6 +170,58 @@ int lwm_blockattn_fwd(const lwm_tensor4* q, const lwm_tensor4* k, const lwm_tens
   p.lse = lse;
   p.mode = 0;
   return hip_status(lwm::launch_attn_fwd(p, q->dtype == LWM_BF16, static_cast<hipStream_t>(stream)), "forward launch");
+}
+
+int lwm_blockattn_fwd_rope(const lwm_tensor4* q, const lwm_tensor4* k, const lwm_tensor4* v, const int32_t* seg_q,
+                           const int32_t* seg_k, int64_t q_offset, int64_t k_offset, int32_t causal, float scale,
+                           const lwm_rope_args* rope, const lwm_tensor4* o, float* lse, const lwm_tensor4* q_rot,
+                           const lwm_tensor4* k_rot, void* stream) {
+  int s;
+  if ((s = check_attention(q, k, v, seg_q, seg_k, q_offset, k_offset, causal))) return s;
+  if (q->dtype != LWM_BF16) return fail(LWM_ERR_UNSUPPORTED, "the fused-RoPE forward is implemented for bf16 only");
+  if ((s = check_tensor(o, "o")) || (s = check_same(q, o, "q", "o", true))) return s;
+  if ((s = check_tensor(k_rot, "k_rot")) || (s = check_same(k, k_rot, "k", "k_rot", true))) return s;
+  if (k_rot->ptr == k->ptr && (k_rot->sB != k->sB || k_rot->sL != k->sL || k_rot->sH != k->sH))
+    return fail(LWM_ERR_INVALID_ARG, "k_rot == k (in place) needs identical strides");
+  if (q_rot) {
+    if ((s = check_tensor(q_rot, "q_rot")) || (s = check_same(q, q_rot, "q", "q_rot", true))) return s;
+    if (q_rot->ptr && q_rot->ptr == q->ptr) return fail(LWM_ERR_INVALID_ARG, "q_rot must not overlap q");
+  }
+  float sc;
+  if ((s = check_scale(scale, q->D, &sc))) return s;
+  if (lse && reinterpret_cast<uintptr_t>(lse) % 4) return fail(LWM_ERR_INVALID_ARG, "lse not 4-byte aligned");
+  lwm::RopeFuse rf;
+  if ((s = check_rope(rope, seg_q != nullptr, &rf))) return s;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  // the keys: one RoPE pass into k_rot (what lwm_rope_apply would do)
+  lwm::RopeParams rp{};
+  rp.x = k->ptr;
+  rp.y = k_rot->ptr;
+  rp.pos = nullptr;
+  rp.seg = rope->restart ? seg_k : nullptr;
+  rp.pos_offset = rope->k_pos_offset;
+  rp.B = (int)k->B; rp.L = (int)k->L; rp.H = (int)k->H; rp.D = (int)k->D;
+  rp.xsB = k->sB; rp.xsL = k->sL; rp.xsH = k->sH;
+  rp.ysB = k_rot->sB; rp.ysL = k_rot->sL; rp.ysH = k_rot->sH;
+  rp.layout = rope->layout;
+  rp.inverse = 0;
+  for (int i = 0; i < rp.D / 2; ++i) rp.inv_freq[i] = rf.inv_freq[i];
+  if ((s = hip_status(lwm::launch_rope(rp, true, st), "rope launch"))) return s;
+  // the queries: rotated inside the forward kernel
+  lwm::FwdParams p{};
+  p.q = q->ptr; p.k = k_rot->ptr; p.v = v->ptr;
+  p.sq = strides(q); p.sk = strides(k_rot); p.sv = strides(v);
+  p.B = (int)q->B; p.H = (int)q->H; p.Lq = (int)q->L; p.Lk = (int)k->L;
+  p.seg_q = seg_q; p.seg_k = seg_k;
+  p.q_offset = q_offset; p.k_offset = k_offset; p.causal = causal;
+  p.scale_log2 = sc * 1.4426950408889634f;
+  p.o = o->ptr; p.so = strides(o);
+  p.lse = lse;
+  p.mode = 0;
+  p.rope = rf;
+  p.q_rot = q_rot ? q_rot->ptr : nullptr;
+  if (q_rot) p.sqr = strides(q_rot);
+  return hip_status(lwm::launch_attn_fwd(p, true, st), "forward launch");
 }
 
 size_t lwm_blockattn_bwd_workspace_size(int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D) {
@@ -226,6 +300,27 @@ int lwm_blockattn_bwd(const lwm_tensor4* q, const lwm_tensor4* k, const lwm_tens
   if ((s = check_tensor(dq, "dq")) || (s = check_same(q, dq, "q", "dq", true))) return s;
   if ((s = check_tensor(dk, "dk")) || (s = check_same(k, dk, "k", "dk", true))) return s;
   if ((s = check_tensor(dv, "dv")) || (s = check_same(v, dv, "v", "dv", true))) return s;
+  p.dq = static_cast<uint16_t*>(dq->ptr);
+  p.dk = static_cast<uint16_t*>(dk->ptr);
+  p.dv = static_cast<uint16_t*>(dv->ptr);
+  p.sdq = strides(dq); p.sdk = strides(dk); p.sdv = strides(dv);
+  return hip_status(lwm::launch_attn_bwd(p, static_cast<hipStream_t>(stream)), "backward launch");
+}
+
+int lwm_blockattn_bwd_rope(const lwm_tensor4* q_rot, const lwm_tensor4* k_rot, const lwm_tensor4* v,
+                           const lwm_tensor4* o, const float* lse, const lwm_tensor4* dout, const int32_t* seg_q,
+                           const int32_t* seg_k, int64_t q_offset, int64_t k_offset, int32_t causal, float scale,
+                           const lwm_rope_args* rope, const lwm_tensor4* dq, const lwm_tensor4* dk,
+                           const lwm_tensor4* dv, void* workspace, size_t workspace_bytes, void* stream) {
+  lwm::BwdParams p;
+  int s;
+  if ((s = prepare_bwd(q_rot, k_rot, v, o, lse, dout, seg_q, seg_k, q_offset, k_offset, causal, scale, workspace,
+                       workspace_bytes, &p)))
+    return s;
+  if ((s = check_tensor(dq, "dq")) || (s = check_same(q_rot, dq, "q_rot", "dq", true))) return s;
+  if ((s = check_tensor(dk, "dk")) || (s = check_same(k_rot, dk, "k_rot", "dk", true))) return s;
+  if ((s = check_tensor(dv, "dv")) || (s = check_same(v, dv, "v", "dv", true))) return s;
+  if ((s = check_rope(rope, seg_q != nullptr, &p.rope))) return s;
   p.dq = static_cast<uint16_t*>(dq->ptr);
   p.dk = static_cast<uint16_t*>(dk->ptr);
   p.dv = static_cast<uint16_t*>(dv->ptr);

@@ -17,12 +17,16 @@
 //    scores in the other orientation (S = Q K^T, each lane owns one key): P and dS feed
 //    dV^T += dO^T P and dK^T += Q^T dS directly; Q^T and dO^T operands come from the row-major tiles
 //    by transposing LDS reads.
+//  With fused RoPE (lwm_blockattn_bwd_rope) the dQ and dK/dV kernels rotate their float32 dQ', dK'
+//  accumulators back by -angle just before the one rounding to bf16, so the stored gradients are
+//  w.r.t. the pre-RoPE Q and K.
 //  Tiles travel HBM -> LDS by buffer loads that write LDS directly (double-buffered).  Recomputing
 //  S and dP in both kernels costs two extra products over the five the method needs; in exchange
 //  no partial dQ is ever written to or reduced through memory.
 
 #include "attn_common.hpp"
 #include "profile.hpp"
+#include "rope_dev.hpp"
 
 namespace lwm {
 namespace {
@@ -263,6 +267,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
     add_rows_f32(stage_w, acc, p.scale, p.dq_acc + b * p.sdqa.b + hh * p.sdqa.h + wr0 * p.sdqa.l, p.sdqa.l,
                  rows_valid);
   } else {
+    if (p.rope.on) {  // dQ' -> dQ (inverse RoPE of the query rows) before the one rounding to bf16
+      const bool restart = segs && p.rope.restart;
+      const int64_t pos = rope_row_position(restart ? p.seg_q + (int64_t)b * p.Lq : nullptr, p.Lq, wr0, restart,
+                                            p.rope.q_pos_offset);
+      rope_unrotate_acc(acc, pos, p.rope, h32);
+    }
     uint8_t* stage_w = reinterpret_cast<uint8_t*>(&sm) + w * (32 * D * 2);
     store_rows_bf16(stage_w, acc, p.scale, p.dq + b * p.sdq.b + hh * p.sdq.h + wr0 * p.sdq.l, p.sdq.l, rows_valid);
   }
@@ -529,6 +539,12 @@ __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams 
     add_rows_f32(stage_w, dk, p.scale, p.dk_acc + b * p.sdka.b + hh * p.sdka.h + wk0 * p.sdka.l, p.sdka.l, rows_valid);
     add_rows_f32(stage_w, dv, 1.f, p.dv_acc + b * p.sdva.b + hh * p.sdva.h + wk0 * p.sdva.l, p.sdva.l, rows_valid);
   } else {
+    if (p.rope.on && qh == 0) {  // dK' -> dK (inverse RoPE of the key rows) before rounding to bf16
+      const bool restart = segs && p.rope.restart;
+      const int64_t pos = rope_row_position(restart ? p.seg_k + (int64_t)b * p.Lk : nullptr, p.Lk, wk0, restart,
+                                            p.rope.k_pos_offset);
+      rope_unrotate_acc(dk, pos, p.rope, h32);
+    }
     uint8_t* stage_w = reinterpret_cast<uint8_t*>(&sm) + w * (32 * D * 2);
     store_rows_bf16(stage_w, dk, p.scale, p.dk + b * p.sdk.b + hh * p.sdk.h + wk0 * p.sdk.l, p.sdk.l, rows_valid);
     store_rows_bf16(stage_w, dv, 1.f, p.dv + b * p.sdv.b + hh * p.sdv.h + wk0 * p.sdv.l, p.sdv.l, rows_valid);

@@ -26,6 +26,11 @@
 //    tile is masked element-wise only when it straddles a boundary or the ragged end (a tile one
 //    wave sees nothing of is computed fully masked: there are few, and the pipeline stays
 //    branch-free).
+//  * Fused RoPE (lwm_blockattn_fwd_rope): q holds the pre-RoPE queries and each wave rotates its
+//    rows' fragments in registers right after loading them (the standalone RoPE kernel's
+//    arithmetic from rope_dev.hpp, so the bits are those of a separate pass), optionally storing
+//    the rotated rows for the backward.  Keys are not rotated here: every query tile streams them
+//    again, and rotating each visit would add a third to the loop's vector work.
 //  * Workgroups are numbered longest-first, and when B*H is a multiple of 8 the (batch, head)
 //    pairs are dealt to the 8 XCDs so the query tiles sharing one head's K/V run on one L2.
 #include <float.h>
@@ -34,6 +39,7 @@
 
 #include "attn_common.hpp"
 #include "profile.hpp"
+#include "rope_dev.hpp"
 
 namespace lwm {
 namespace {
@@ -76,8 +82,9 @@ struct SmemSp {
 };
 static_assert(sizeof(SmemSp) <= 80 * 1024, "two workgroups per CU must fit in LDS");
 
-template <bool kSegs, bool kRing>
+template <bool kSegs, bool kRing, bool kRope = false>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdParams p) {
+  static_assert(!(kRing && kRope), "the ring step takes rotated queries");
   constexpr int BM = kWaves * 32;
   __shared__ __attribute__((aligned(1024))) SmemSp sm;
 
@@ -121,6 +128,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdParams p)
     u32x4 v = {0u, 0u, 0u, 0u};
     if (qrow < p.Lq) v = *reinterpret_cast<const u32x4*>(qg + qrow * p.sq.l + s * 16 + h32 * 8);
     qreg[s] = as_bf16x8(v);
+  }
+  if constexpr (kRope) {
+    // q holds the pre-RoPE rows: rotate them here (the standalone RoPE kernel's arithmetic, so
+    // the bits equal those of a separate RoPE pass) and hand the rotated rows on if asked
+    const bool restart = kSegs && p.rope.restart;
+    const int64_t pos = rope_row_position(restart ? p.seg_q + (int64_t)b * p.Lq : nullptr, p.Lq, wr0, restart,
+                                          p.rope.q_pos_offset);
+    rope_rotate_frags(qreg, pos, p.rope, h32);
+    if (p.q_rot && qrow < p.Lq) {
+      uint16_t* qr = static_cast<uint16_t*>(p.q_rot) + b * p.sqr.b + hh * p.sqr.h + (int64_t)qrow * p.sqr.l;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) *reinterpret_cast<u32x4*>(qr + s * 16 + h32 * 8) = as_u32x4(qreg[s]);
+    }
   }
 
   // running state: O^T accumulators, row max m (log2-scaled), partial row sum l (this half's keys)
@@ -543,6 +563,9 @@ hipError_t launch_attn_fwd(const FwdParams& p, bool bf16, hipStream_t stream) {
     if (p.mode == 1) {
       if (segs) LWM_LAUNCH("ring_step_bf16", (attn_fwd_bf16_kernel<true, true>), grid, block, stream, p);
       else LWM_LAUNCH("ring_step_bf16", (attn_fwd_bf16_kernel<false, true>), grid, block, stream, p);
+    } else if (p.rope.on) {
+      if (segs) LWM_LAUNCH("attn_fwd_rope_bf16", (attn_fwd_bf16_kernel<true, false, true>), grid, block, stream, p);
+      else LWM_LAUNCH("attn_fwd_rope_bf16", (attn_fwd_bf16_kernel<false, false, true>), grid, block, stream, p);
     } else {
       if (segs) LWM_LAUNCH("attn_fwd_bf16", (attn_fwd_bf16_kernel<true, false>), grid, block, stream, p);
       else LWM_LAUNCH("attn_fwd_bf16", (attn_fwd_bf16_kernel<false, false>), grid, block, stream, p);

@@ -28,6 +28,17 @@ struct Strides {
   int64_t b, l, h;
 };
 
+// RoPE applied inside the attention kernels.  Row t of the query (key) operand has position
+// q_pos_offset + t (k_pos_offset + t), or that offset plus t minus the first index of t's segment
+// when `restart` is set; inv_freq[i] = theta^(-2i/D).
+struct RopeFuse {
+  int on;       // 0: the operands are already rotated, nothing is fused
+  int layout;   // 0: (i, i + D/2), 1: (2i, 2i + 1)
+  int restart;  // positions restart at each segment (segment ids given)
+  int64_t q_pos_offset, k_pos_offset;
+  double inv_freq[kHeadDim / 2];
+};
+
 // Forward / ring-step attention.  mode 0: fresh state, writes o (+ lse).  mode 1: ring step,
 // state read from and written back to o_acc / lse_acc, o optional (bf16 copy of the result).
 struct FwdParams {
@@ -48,6 +59,11 @@ struct FwdParams {
   Strides soa;
   float* lse_acc;
   int mode;
+  // rope.on: q holds the pre-RoPE queries; each workgroup rotates its rows as it loads them and,
+  // when q_rot is set, stores the rotated rows there (bf16 path, fresh state only)
+  RopeFuse rope;
+  void* q_rot;
+  Strides sqr;
 };
 
 struct BwdParams {
@@ -77,6 +93,9 @@ struct BwdParams {
   float* dk_acc;
   float* dv_acc;
   Strides sdqa, sdka, sdva;
+  // rope.on: dq and dk are rotated back (inverse RoPE) before they are stored, so they are
+  // gradients w.r.t. the pre-RoPE Q and K (stored outputs only, not the ring accumulators)
+  RopeFuse rope;
 };
 
 // Blockwise feed-forward block (bf16): y = (silu(x W_gate^T) * (x W_up^T)) W_down^T over chunks

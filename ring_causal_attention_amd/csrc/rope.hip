@@ -4,12 +4,12 @@
 //
 // HBM-bound: every element is read and written once.  A workgroup owns kTok consecutive tokens
 // of one batch row.  It first forms the kTok x D/2 angles once (double precision: position times
-// inv_freq, reduced modulo 2*pi) and their sine/cosine (single precision) in LDS, then streams
+// inv_freq, reduced modulo pi/2) and their sine/cosine (rounded to single precision) in LDS, then streams
 // all H heads of those tokens with 16-byte vector loads and stores, so the trigonometry is shared
 // by every head instead of being repeated per element.
-#include "common.hpp"
 #include "kernels.hpp"
 #include "profile.hpp"
+#include "rope_dev.hpp"
 
 namespace lwm {
 namespace {
@@ -73,9 +73,6 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(RopeParams p) {
   const int ntok = min(kTok, p.L - t0);
 
   // ---- phase 1: angles (double), sin/cos (float) for kTok tokens x D/2 pairs
-  const double two_pi_hi = 6.283185307179586;          // nearest double to 2*pi
-  const double two_pi_lo = 2.4492935982947064e-16;     // 2*pi - two_pi_hi
-  const double inv_two_pi = 0.15915494309189535;
   for (int e = threadIdx.x; e < ntok * half; e += kThreads) {
     const int tt = e / half, i = e - tt * half;
     const int t = t0 + tt;
@@ -83,13 +80,8 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(RopeParams p) {
     if (p.pos) pos = p.pos[(int64_t)b * p.L + t];
     else if (p.seg) pos = t - segment_start(p.seg + (int64_t)b * p.L, t);
     else pos = t;
-    pos += p.pos_offset;
-    const double ang = (double)pos * p.inv_freq[i];
-    const double k = rint(ang * inv_two_pi);
-    double r = fma(-k, two_pi_hi, ang);
-    r = fma(-k, two_pi_lo, r);
     float s, c;
-    sincosf((float)r, &s, &c);
+    rope_cos_sin(pos + p.pos_offset, p.inv_freq[i], c, s);
     cs[tt][i] = make_float2(c, p.inverse ? -s : s);
   }
   __syncthreads();
@@ -115,10 +107,7 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(RopeParams p) {
 #pragma unroll
       for (int j = 0; j < N; ++j) {
         const float2 r = cs[tt][c * N + j];
-        const float ra = a[j] * r.x - bb[j] * r.y;
-        const float rb = a[j] * r.y + bb[j] * r.x;
-        a[j] = ra;
-        bb[j] = rb;
+        rope_rotate(a[j], bb[j], r.x, r.y, a[j], bb[j]);
       }
       Vec<T>::store(ys, a);
       Vec<T>::store(ys + half, bb);
@@ -139,9 +128,7 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(RopeParams p) {
 #pragma unroll
       for (int j = 0; j < N / 2; ++j) {
         const float2 r = cs[tt][c * (N / 2) + j];
-        const float u = a[2 * j], w = a[2 * j + 1];
-        a[2 * j] = u * r.x - w * r.y;
-        a[2 * j + 1] = u * r.y + w * r.x;
+        rope_rotate(a[2 * j], a[2 * j + 1], r.x, r.y, a[2 * j], a[2 * j + 1]);
       }
       Vec<T>::store(ys, a);
     }

@@ -33,9 +33,15 @@ class Tensor4(ctypes.Structure):
                 ("sB", ctypes.c_int64), ("sL", ctypes.c_int64), ("sH", ctypes.c_int64)]
 
 
+class RopeArgs(ctypes.Structure):
+    _fields_ = [("theta", ctypes.c_double), ("layout", ctypes.c_int32), ("restart", ctypes.c_int32),
+                ("q_pos_offset", ctypes.c_int64), ("k_pos_offset", ctypes.c_int64)]
+
+
 _lib = None
 EXPORTS = ["lwm_abi_version", "lwm_last_error", "lwm_rope_apply", "lwm_blockattn_fwd",
-           "lwm_blockattn_bwd_workspace_size", "lwm_blockattn_bwd", "lwm_ring_step", "lwm_ring_step_bwd",
+           "lwm_blockattn_bwd_workspace_size", "lwm_blockattn_bwd", "lwm_blockattn_fwd_rope",
+           "lwm_blockattn_bwd_rope", "lwm_ring_step", "lwm_ring_step_bwd",
            "lwm_blockwise_ffn_workspace_size", "lwm_blockwise_ffn", "lwm_profile_enable", "lwm_profile_reset", "lwm_profile_count", "lwm_profile_get"]
 
 
@@ -61,6 +67,12 @@ def lib() -> ctypes.CDLL:
     L.lwm_blockattn_bwd_workspace_size.argtypes = [I64, I64, I64, I64, I64]
     L.lwm_blockattn_bwd.restype = ctypes.c_int
     L.lwm_blockattn_bwd.argtypes = [P, P, P, P, VP, P, VP, VP, I64, I64, I32, F32, P, P, P, VP, ctypes.c_size_t, VP]
+    R = ctypes.POINTER(RopeArgs)
+    L.lwm_blockattn_fwd_rope.restype = ctypes.c_int
+    L.lwm_blockattn_fwd_rope.argtypes = [P, P, P, VP, VP, I64, I64, I32, F32, R, P, VP, P, P, VP]
+    L.lwm_blockattn_bwd_rope.restype = ctypes.c_int
+    L.lwm_blockattn_bwd_rope.argtypes = [P, P, P, P, VP, P, VP, VP, I64, I64, I32, F32, R, P, P, P, VP,
+                                         ctypes.c_size_t, VP]
     L.lwm_ring_step.restype = ctypes.c_int
     L.lwm_ring_step.argtypes = [P, P, P, VP, VP, I64, I64, I32, F32, P, VP, P, VP]
     L.lwm_ring_step_bwd.restype = ctypes.c_int
@@ -168,6 +180,51 @@ def lwm_blockattn_bwd(q, k, v, o, lse, dout, seg_q=None, seg_k=None, q_offset=0,
                                    int(k_offset), int(bool(causal)), float(scale), _ref(tensor4(dq)),
                                    _ref(tensor4(dk)), _ref(tensor4(dv)), _ptr(workspace),
                                    workspace.numel() * workspace.element_size(), _stream(q)))
+    return dq, dk, dv
+
+
+def rope_args(theta, layout="half", restart=False, q_pos_offset=0, k_pos_offset=0) -> RopeArgs:
+    """The RoPE descriptor of the fused entry points (positions restart per segment if restart)."""
+    return RopeArgs(float(theta), LAYOUTS[layout], int(bool(restart)), int(q_pos_offset), int(k_pos_offset))
+
+
+def lwm_blockattn_fwd_rope(q, k, v, theta, seg_q=None, seg_k=None, q_offset=0, k_offset=0, causal=True, scale=0.0,
+                           layout="half", restart=False, q_pos_offset=0, k_pos_offset=0, o=None, lse=None,
+                           q_rot=None, k_rot=None, want_q_rot=True):
+    """Forward from the pre-RoPE q, k (RoPE inside the call); returns (o, lse, q_rot, k_rot).
+    q_rot is None when want_q_rot is False and no buffer is given."""
+    B, Lq, H, _ = q.shape
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device) if lse is None else lse
+    k_rot = torch.empty_like(k) if k_rot is None else k_rot
+    if q_rot is None and want_q_rot:
+        q_rot = torch.empty_like(q)
+    ra = rope_args(theta, layout, restart, q_pos_offset, k_pos_offset)
+    _check(lib().lwm_blockattn_fwd_rope(_ref(tensor4(q)), _ref(tensor4(k)), _ref(tensor4(v)), _ptr(_seg(seg_q)),
+                                        _ptr(_seg(seg_k)), int(q_offset), int(k_offset), int(bool(causal)),
+                                        float(scale), ctypes.byref(ra), _ref(tensor4(o)), _ptr(lse),
+                                        _ref(tensor4(q_rot)), _ref(tensor4(k_rot)), _stream(q)))
+    return o, lse, q_rot, k_rot
+
+
+def lwm_blockattn_bwd_rope(q_rot, k_rot, v, o, lse, dout, theta, seg_q=None, seg_k=None, q_offset=0, k_offset=0,
+                           causal=True, scale=0.0, layout="half", restart=False, q_pos_offset=0, k_pos_offset=0,
+                           dq=None, dk=None, dv=None, workspace=None):
+    """Backward with the inverse RoPE inside the call; returns (dq, dk, dv) w.r.t. the pre-RoPE Q, K."""
+    B, Lq, H, D = q_rot.shape
+    dq = torch.empty_like(q_rot) if dq is None else dq
+    dk = torch.empty_like(k_rot) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if workspace is None:
+        workspace = torch.empty(lwm_blockattn_bwd_workspace_size(B, H, Lq, k_rot.shape[1], D), dtype=torch.uint8,
+                                device=q_rot.device)
+    ra = rope_args(theta, layout, restart, q_pos_offset, k_pos_offset)
+    _check(lib().lwm_blockattn_bwd_rope(_ref(tensor4(q_rot)), _ref(tensor4(k_rot)), _ref(tensor4(v)),
+                                        _ref(tensor4(o)), _ptr(lse), _ref(tensor4(dout)), _ptr(_seg(seg_q)),
+                                        _ptr(_seg(seg_k)), int(q_offset), int(k_offset), int(bool(causal)),
+                                        float(scale), ctypes.byref(ra), _ref(tensor4(dq)), _ref(tensor4(dk)),
+                                        _ref(tensor4(dv)), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _stream(q_rot)))
     return dq, dk, dv
 
 

@@ -7,6 +7,8 @@
 * ``attention_forward`` - RoPE on Q and K, then the blockwise forward.
 * ``training_step`` - RoPE, forward (saving lse), backward, and inverse RoPE of dQ', dK' so the
   gradients are w.r.t. the pre-RoPE Q and K.
+* ``training_step_fused`` - the same step with RoPE inside the attention calls: the forward
+  rotates Q as it loads it (K by one pass) and the backward rotates dQ', dK' back before storing.
 """
 from __future__ import annotations
 
@@ -118,4 +120,20 @@ def training_step(q, k, v, dout, theta, seg=None, layout="half", causal=True, sc
                           scale=scale, dq=bufs.dq, dk=bufs.dk, dv=bufs.dv, workspace=bufs.workspace)
     lwm.lwm_rope_apply(bufs.dq, bufs.dq, seg=seg, theta=theta, layout=layout, inverse=True)
     lwm.lwm_rope_apply(bufs.dk, bufs.dk, seg=seg, theta=theta, layout=layout, inverse=True)
+    return bufs.o, bufs.lse, bufs.dq, bufs.dk, bufs.dv
+
+
+def training_step_fused(q, k, v, dout, theta, seg=None, layout="half", causal=True, scale=0.0, buffers=None):
+    """``training_step`` through the fused-RoPE entry points; returns (o, lse, dq, dk, dv).
+
+    Positions restart per segment when ``seg`` is given.  Two calls (forward, backward) and five
+    kernels instead of seven: no separate RoPE pass over Q and no inverse-RoPE passes over dQ and dK.
+    """
+    bufs = buffers if buffers is not None else TrainStepBuffers(q, k)
+    restart = seg is not None
+    lwm.lwm_blockattn_fwd_rope(q, k, v, theta, seg_q=seg, seg_k=seg, causal=causal, scale=scale, layout=layout,
+                               restart=restart, o=bufs.o, lse=bufs.lse, q_rot=bufs.qr, k_rot=bufs.kr)
+    lwm.lwm_blockattn_bwd_rope(bufs.qr, bufs.kr, v, bufs.o, bufs.lse, dout, theta, seg_q=seg, seg_k=seg, causal=causal,
+                               scale=scale, layout=layout, restart=restart, dq=bufs.dq, dk=bufs.dk, dv=bufs.dv,
+                               workspace=bufs.workspace)
     return bufs.o, bufs.lse, bufs.dq, bufs.dk, bufs.dv

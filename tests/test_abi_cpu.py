@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol():
     assert set(names) == set(lwm.EXPORTS), names
     for n in names:
         assert hasattr(L, n), n
-    assert L.lwm_abi_version() == 3
+    assert L.lwm_abi_version() == 4
     assert L.lwm_last_error() == b""
 
 
@@ -123,6 +123,51 @@ def test_rope_validation():
                          ((r(t4(D=24)), r(t4(D=24)), None, None, 0, 1e4, 0, 0, None), -2),
                          ((r(x), r(x), None, None, 0, 1e4, 0, 3, None), -1)]:
         assert L.lwm_rope_apply(*args) == status, args
+
+
+def test_fused_rope_validation():
+    """The fused-RoPE entry points check the RoPE descriptor and the extra outputs before any launch."""
+    L = _lib()
+    r = ctypes.byref
+    q = t4()
+    good = lwm.RopeArgs(1e6, 0, 0, 0, 0)
+
+    def fwd_rope(rope=good, q_rot=None, k_rot=q, seg=None, dtype=0, qp=16):
+        x = t4(dtype=dtype, ptr=qp)
+        st = L.lwm_blockattn_fwd_rope(r(x), r(t4(dtype=dtype)), r(t4(dtype=dtype)), seg, seg, 0, 0, 1, 0.0,
+                                      None if rope is None else r(rope), r(t4(dtype=dtype)), None,
+                                      None if q_rot is None else r(q_rot), None if k_rot is None else r(k_rot), None)
+        return st, L.lwm_last_error().decode()
+
+    for kwargs, status, needle in [
+        ({"rope": None}, -1, "rope is NULL"),
+        ({"rope": lwm.RopeArgs(0.0, 0, 0, 0, 0)}, -1, "theta"),
+        ({"rope": lwm.RopeArgs(float("inf"), 0, 0, 0, 0)}, -1, "theta"),
+        ({"rope": lwm.RopeArgs(1e6, 2, 0, 0, 0)}, -1, "layout"),
+        ({"rope": lwm.RopeArgs(1e6, 0, 2, 0, 0)}, -1, "restart"),
+        ({"rope": lwm.RopeArgs(1e6, 0, 1, 0, 0)}, -1, "restart = 1 needs"),
+        ({"rope": lwm.RopeArgs(1e6, 0, 0, 1 << 41, 0)}, -1, "offsets"),
+        ({"k_rot": None}, -1, "k_rot"),
+        ({"k_rot": t4(L=9)}, -1, "mismatch"),
+        ({"q_rot": t4(ptr=16)}, -1, "overlap"),
+        ({"q_rot": t4(H=3)}, -1, "mismatch"),
+        ({"dtype": 1, "k_rot": t4(dtype=1)}, -2, "bf16"),
+    ]:
+        st, msg = fwd_rope(**kwargs)
+        assert st == status and needle in msg, (kwargs, st, msg)
+    # in-place key rotation (k_rot == k) needs the same strides
+    st, msg = fwd_rope(k_rot=t4(sH=256, sL=512, sB=4096))
+    assert st == -1 and "strides" in msg, (st, msg)
+    ws = L.lwm_blockattn_bwd_workspace_size(1, 2, 8, 8, 128)
+
+    def bwd_rope(rope=good, seg=None, nbytes=ws, dk=q):
+        return L.lwm_blockattn_bwd_rope(r(q), r(q), r(q), r(q), 16, r(q), seg, seg, 0, 0, 1, 0.0,
+                                        None if rope is None else r(rope), r(q), r(dk), r(q), 256, nbytes, None)
+
+    assert bwd_rope(rope=None) == -1 and "rope" in L.lwm_last_error().decode()
+    assert bwd_rope(rope=lwm.RopeArgs(1e6, 0, 1, 0, 0)) == -1 and "restart" in L.lwm_last_error().decode()
+    assert bwd_rope(nbytes=ws - 1) == -3
+    assert bwd_rope(dk=t4(L=9)) == -1 and "mismatch" in L.lwm_last_error().decode()
 
 
 def test_ffn_validation():
