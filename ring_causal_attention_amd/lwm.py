@@ -110,9 +110,11 @@ def tensor4(t: torch.Tensor | None) -> Tensor4 | None:
         dt = LWM_FP32
     else:
         raise ValueError(f"unsupported dtype {t.dtype}")
+    B, L, H, D = t.shape
+    if t.numel() == 0:  # no element is addressed: describe it with contiguous strides
+        return Tensor4(t.data_ptr(), dt, 0, B, L, H, D, L * H * D, H * D, D)
     if t.shape[3] > 1 and t.stride(3) != 1:
         raise ValueError("the feature dimension must be contiguous")
-    B, L, H, D = t.shape
     return Tensor4(t.data_ptr(), dt, 0, B, L, H, D, t.stride(0), t.stride(1), t.stride(2))
 
 
