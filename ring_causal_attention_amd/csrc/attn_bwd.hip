@@ -33,18 +33,6 @@ namespace {
 
 constexpr int kTileBytes = 64 * 256;  // 64 rows x 128 bf16
 
-// Scheduling pattern for the preceding straight-line code: N groups of one MFMA, NV VALU
-// instructions and ND LDS reads, so VALU work is issued while each MFMA runs.
-template <int N, int NV, int ND>
-__device__ __forceinline__ void interleave() {
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);  // VALU
-    __builtin_amdgcn_sched_group_barrier(0x100, ND, 0);  // LDS read
-  }
-}
-
 // ------------------------------------------------------------------------------ delta
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
   const int64_t rows = (int64_t)p.B * p.Lq * p.H;

@@ -11,45 +11,6 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
 constexpr int D = kHeadDim;
 
-// ---------------------------------------------------------------- LDS layouts
-// Row-major tile of 128 features (16 chunks of 16 bytes per row): chunk c of row r lives at
-// r*16 + (c ^ (r & 7)), so the 8 rows read together by an MFMA operand fetch hit 8 distinct chunks.
-__device__ __forceinline__ int rm_index(int r, int c) { return r * 16 + (c ^ (r & 7)); }
-
-// Transposed tile (feature-major): row d holds the tile's rows (keys or queries) in the order
-// that makes an MFMA accumulator's rows contiguous per lane half: inside each group of 16,
-// offset o sits at position ((o>>2)&1)*8 + (o>>3)*4 + (o&3), i.e. {0..3, 8..11} then
-// {4..7, 12..15}.  A 64-row tile has 8 chunks per feature row, a 32-row tile 4; the chunk
-// index is XOR-swizzled by feature so that 8 consecutive features hit distinct banks.
-__device__ __forceinline__ int group_pos(int o) { return ((o >> 2) & 1) * 8 + (o >> 3) * 4 + (o & 3); }
-__device__ __forceinline__ int t64_index(int d, int chunk) { return d * 8 + (chunk ^ ((d & 7) ^ ((d >> 3) & 7))); }
-__device__ __forceinline__ int t32_index(int d, int chunk) { return d * 4 + (chunk ^ ((d >> 1) & 3)); }
-
-// Write 4 consecutive rows (4q .. 4q+3, q = quad index) x 8 features (8*dg .. 8*dg+7), held as
-// four 16-byte row pieces, into a transposed tile.  The quad's 4 values of one feature are 8
-// contiguous bytes (one u32x2 store per feature).
-template <int ROWS>
-__device__ __forceinline__ void write_transposed_quad(u32x4* tile, int quad, int dg, const u32x4 (&rows)[4]) {
-  const int grp = quad >> 2, qin = quad & 3;
-  const int pos = grp * 16 + (qin & 1) * 8 + (qin >> 1) * 4;  // group_pos of the quad's first row
-  const int chunk = pos >> 3, sub = (pos >> 2) & 1;
-#pragma unroll
-  for (int jd = 0; jd < 8; ++jd) {
-    const int d = dg * 8 + jd;
-    const int word = jd >> 1;
-    uint32_t w0, w1;
-    if (jd & 1) {
-      w0 = (rows[0][word] >> 16) | (rows[1][word] & 0xffff0000u);
-      w1 = (rows[2][word] >> 16) | (rows[3][word] & 0xffff0000u);
-    } else {
-      w0 = (rows[0][word] & 0xffffu) | (rows[1][word] << 16);
-      w1 = (rows[2][word] & 0xffffu) | (rows[3][word] << 16);
-    }
-    const int idx = ROWS == 64 ? t64_index(d, chunk) : t32_index(d, chunk);
-    reinterpret_cast<u32x2*>(&tile[idx])[sub] = u32x2{w0, w1};
-  }
-}
-
 // ---------------------------------------------------------------- direct-to-LDS tiles (CDNA4)
 // A tile is R rows (keys or queries) x 128 bf16 features, row-major, one 256-byte row per key:
 // exactly one row of the 64 x 4-byte LDS banks.  The sixteen 16-byte chunks of row r are stored
@@ -123,8 +84,6 @@ __device__ __forceinline__ void tr_offsets(int lane, int db, int& off_lo, int& o
   off_lo = row_lo * 256 + ((chunk ^ swz16(row_lo)) << 4) + sub;
   off_hi = row_hi * 256 + ((chunk ^ swz16(row_hi)) << 4) + sub;
 }
-// Byte offset of the 16-byte chunk `c` of row `row` in a swizzled tile (ds_read_b128 operand).
-__device__ __forceinline__ int rm_offset(int row, int c) { return row * 256 + ((c ^ swz16(row & 15)) << 4); }
 
 // ---------------------------------------------------------------- workgroup order
 // Grid position -> (batch*head, tile).  `descending` numbers tiles from the last one (causal
