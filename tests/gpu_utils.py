@@ -21,6 +21,12 @@ def note(msg: str):
     sys.stdout.flush()
 
 
+def report(case: str, **values):
+    """Print the errors a parity check measured (shown with pytest -s), one line per check."""
+    txt = " ".join(f"{k}={v:.3g}" if isinstance(v, float) else f"{k}={v}" for k, v in values.items())
+    print(f"[parity] {case} {txt}", flush=True)
+
+
 def dev(x: np.ndarray, dtype: str) -> torch.Tensor:
     """float32 host array -> device tensor; bf16 rounds to nearest even exactly like synth."""
     if dtype == "bf16":

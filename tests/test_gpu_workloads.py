@@ -12,7 +12,7 @@ import oracle
 from ring_causal_attention_amd import configs, lwm, path, workloads
 from ring_causal_attention_amd.synth import round_to_bf16
 from tests.gpu_utils import (BF16_MAX_ABS, BF16_MEAN_ABS, FP32_MAX_ABS, GRAD_REL_FRO, LSE_BF16, errors, host,
-                             need_gpu, note, rel_fro)
+                             need_gpu, note, rel_fro, report)
 
 pytestmark = pytest.mark.gpu
 W = configs.WORKLOADS
@@ -56,9 +56,10 @@ def check_rows(o_dev, lse_dev, ref_o, ref_l, rows, dtype, heads=None):
         assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (mx, mean)
     else:
         assert mx <= FP32_MAX_ABS, mx
+    lmx = float(np.max(np.abs(gl - ref_l))) if gl is not None else None
     if gl is not None:
-        assert np.max(np.abs(gl - ref_l)) <= (LSE_BF16 if dtype == "bf16" else 1e-5)
-    return mx, mean
+        assert lmx <= (LSE_BF16 if dtype == "bf16" else 1e-5)
+    return mx, mean, lmx
 
 
 def test_causal_fp32_L1024_full():
@@ -72,9 +73,11 @@ def test_causal_fp32_L1024_full():
     pos = oracle.positions(w.B, w.Lq)
     qr, kr = oracle.rope(exact(h["q"], "fp32"), pos, w.theta), oracle.rope(exact(h["k"], "fp32"), pos, w.theta)
     ro, rl = oracle.attention_fwd(qr, kr, exact(h["v"], "fp32"))
-    mx, _ = errors(host(o), ro)
+    mx, mean = errors(host(o), ro)
+    lmx = float(np.max(np.abs(host(lse) - rl)))
+    report(w.name, rows="all", o_max_abs=mx, o_mean_abs=mean, lse_max_abs=lmx)
     assert mx <= FP32_MAX_ABS, mx
-    assert np.max(np.abs(host(lse) - rl)) <= 1e-5
+    assert lmx <= 1e-5
 
 
 def test_llama7b_fwd_L32768_sampled():
@@ -89,7 +92,8 @@ def test_llama7b_fwd_L32768_sampled():
     rows = sample_rows(w.Lq, seed=2)
     pos = oracle.positions(w.B, w.Lq)
     ro, rl = oracle_rows(h["q"], h["k"], h["v"], rows, w.theta, "bf16", pos, pos)
-    check_rows(o, lse, ro, rl, rows, "bf16")
+    mx, mean, lmx = check_rows(o, lse, ro, rl, rows, "bf16")
+    report(w.name, rows=len(rows), o_max_abs=mx, o_mean_abs=mean, lse_max_abs=lmx)
     # row 0 sees only key 0: O_0 = V_0 exactly
     assert torch.equal(o[:, 0].float(), d["v"][:, 0].float())
 
@@ -108,7 +112,8 @@ def test_packed_L65536_sampled():
     rows = sample_rows(w.Lq, extra=list(starts) + list(ends), seed=3)
     pos = oracle.positions(w.B, w.Lq, 0, h["seg"])
     ro, rl = oracle_rows(h["q"], h["k"], h["v"], rows, w.theta, "bf16", pos, pos, seg=h["seg"])
-    check_rows(o, lse, ro, rl, rows, "bf16")
+    mx, mean, lmx = check_rows(o, lse, ro, rl, rows, "bf16")
+    report(w.name, rows=len(rows), o_max_abs=mx, o_mean_abs=mean, lse_max_abs=lmx)
     # every segment start returns its own V row bit for bit
     assert torch.equal(o[:, starts].float(), d["v"][:, starts].float())
 
@@ -145,9 +150,12 @@ def test_packed_L65536_training_step_one_head():
         start = b
     assert start == w.Lq
     mx, mean = errors(host(o[:, :, hh:hh + 1]), ro)
+    errs = {name: rel_fro(host(g[:, :, hh:hh + 1]), ref) for name, g, ref in (("dq", dq, rdq), ("dk", dk, rdk),
+                                                                            ("dv", dv, rdv))}
+    report(w.name + "_train", head=hh, o_max_abs=mx, o_mean_abs=mean, **{f"{k}_rel_fro": v for k, v in errs.items()},
+           sum_dv_vs_sum_do=float(np.linalg.norm(sdv - sdo) / np.linalg.norm(sdo)))
     assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (mx, mean)
-    for name, g, ref in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
-        e = rel_fro(host(g[:, :, hh:hh + 1]), ref)
+    for name, e in errs.items():
         assert e <= GRAD_REL_FRO, (name, e)
 
 
@@ -170,7 +178,8 @@ def test_ring_share_1M_sampled():
     pos_k = oracle.positions(w.B, k_all.shape[1])
     ro, rl = oracle_rows(h["q"], k_all, v_all, rows, w.theta, "bf16", pos_q, pos_k, q_offset=w.q_offset,
                          heads=heads)
-    check_rows(o, lse, ro, rl, rows, "bf16", heads=heads)
+    mx, mean, lmx = check_rows(o, lse, ro, rl, rows, "bf16", heads=heads)
+    report(w.name, rows=len(rows), heads=len(heads), o_max_abs=mx, o_mean_abs=mean, lse_max_abs=lmx)
 
 
 def test_ring_share_1M_backward_sampled():
@@ -211,6 +220,8 @@ def test_ring_share_1M_backward_sampled():
                                              rl[:, :, n:n + 1], dorow, None, None, w.q_offset + row, j * S, True)
             ref[:, n] += dqj[:, 0]
     got = host(dq_acc[:, rows][:, :, heads])
+    report(w.name + "_backward", rows=len(rows), heads=len(heads), dq_rel_fro=rel_fro(got, ref),
+           sum_dv_vs_sum_do=float(np.linalg.norm(sdv - sdo) / np.linalg.norm(sdo)))
     assert rel_fro(got, ref) <= GRAD_REL_FRO, rel_fro(got, ref)
 
 
@@ -235,7 +246,12 @@ def test_train_step_L32768_one_head():
     ro, rl, rdq, rdk, rdv = oracle.training_step(sl(h["q"]), sl(h["k"]), sl(h["v"]), sl(h["do"]), pos, pos,
                                                  w.theta, "half")
     mx, mean = errors(host(o[:, :, hh:hh + 1]), ro)
+    lmx = float(np.max(np.abs(host(lse[:, hh:hh + 1]) - rl)))
+    errs = {name: rel_fro(host(g[:, :, hh:hh + 1]), ref) for name, g, ref in (("dq", dq, rdq), ("dk", dk, rdk),
+                                                                            ("dv", dv, rdv))}
+    report(w.name, head=hh, o_max_abs=mx, o_mean_abs=mean, lse_max_abs=lmx,
+           **{f"{k}_rel_fro": v for k, v in errs.items()},
+           sum_dv_vs_sum_do=float(np.linalg.norm(sdv - sdo) / np.linalg.norm(sdo)))
     assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (mx, mean)
-    for name, g, ref in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
-        e = rel_fro(host(g[:, :, hh:hh + 1]), ref)
+    for name, e in errs.items():
         assert e <= GRAD_REL_FRO, (name, e)
