@@ -24,6 +24,8 @@
 //  S and dP in both kernels costs two extra products over the five the method needs; in exchange
 //  no partial dQ is ever written to or reduced through memory.
 
+#include <type_traits>
+
 #include "attn_common.hpp"
 #include "profile.hpp"
 #include "rope_dev.hpp"
@@ -274,19 +276,39 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
 // the end.  The workgroup's K and V tiles sit in LDS for the whole pass.
 constexpr int BQ = 64;   // queries per tile
 constexpr int kDkdvWaves = 8;
-struct SmemDkdv {
-  uint8_t qo[2][2][kTileBytes];   // [stage][Q, dO] row-major swizzled
-  uint8_t kv[2][2 * kTileBytes];  // [K, V] of the workgroup's 128 keys, row-major swizzled
-  float lse2[2][BQ];
-  float dlt[2][BQ];
-  int32_t seg[2][BQ];
+// One stage of the query-tile ring: the Q and dO rows of 64 queries (row-major swizzled) and the
+// queries' lse * log2(e), delta and segment ids.  The two stages and the workgroup's K / V rows are
+// LDS objects of their own, and the tile loop is unrolled by two so that every access names its
+// stage at compile time: the compiler makes a transposing LDS read wait for every load into LDS in
+// flight unless it can tell that the read's object differs from theirs, and the next tile's loads
+// are in flight for most of a step.
+struct StageQO {
+  uint8_t q[kTileBytes];
+  uint8_t o[kTileBytes];
+  float lse2[BQ];
+  float dlt[BQ];
+  int32_t seg[BQ];
 };
-static_assert(sizeof(SmemDkdv) >= 4 * 32 * D * 4 * 2, "partial-sum exchange must fit");
-static_assert(sizeof(SmemDkdv) >= kDkdvWaves * 32 * D * 4, "epilogue staging (float32 rows) must fit");
+constexpr int kKVBytes = 4 * kTileBytes;  // K (128 rows) then V (128 rows)
+// after the loop: the partial-sum exchange (dK^T partials in the K/V area, dV^T partials in the two
+// stages' Q / dO areas) and each wave's epilogue staging rows (16 KB: waves 0..3 in the K/V area,
+// 4..7 in the stages) reuse the same three objects
+static_assert(kKVBytes == 4 * 4 * 4 * 64 * 16, "dK partials of 4 key blocks fill the K/V area");
+static_assert(kTileBytes == 4 * 4 * 64 * 16, "one feature block of dV partials fills a Q or dO area");
+static_assert(kTileBytes >= 32 * D * 4, "a wave's staging rows (float32) fit a Q or dO area");
+
+template <int S>
+using StageC = std::integral_constant<int, S>;
 
 __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int BK = 128;
-  __shared__ __attribute__((aligned(1024))) SmemDkdv sm;
+  __shared__ __attribute__((aligned(1024))) StageQO lds_qo0;
+  __shared__ __attribute__((aligned(1024))) StageQO lds_qo1;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_kv[kKVBytes];
+  auto stage = [&](auto sc) __attribute__((always_inline)) -> StageQO& {
+    if constexpr (decltype(sc)::value == 0) return lds_qo0;
+    else return lds_qo1;
+  };
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c32 = lane & 31, h32 = lane >> 5;
   const int kb = w & 3, qh = w >> 2;  // key block of 32, query half of each 64-query tile
@@ -334,12 +356,12 @@ __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams 
       const int blk = w * 4 + r;
       const int row = blk * 4 + (lane >> 4);
       const int c = (lane & 15) ^ swz16(row);
-      load_lds16(rk, &sm.kv[0][blk * 1024], (int)(row * klb) + c * 16);
-      load_lds16(rv, &sm.kv[1][blk * 1024], (int)(row * vlb) + c * 16);
+      load_lds16(rk, &lds_kv[blk * 1024], (int)(row * klb) + c * 16);
+      load_lds16(rv, &lds_kv[2 * kTileBytes + blk * 1024], (int)(row * vlb) + c * 16);
     }
   }
-  const uint8_t* kw = sm.kv[0] + kb * 8192;  // this wave's 32 keys
-  const uint8_t* vw = sm.kv[1] + kb * 8192;
+  const uint8_t* kw = lds_kv + kb * 8192;  // this wave's 32 keys
+  const uint8_t* vw = lds_kv + 2 * kTileBytes + kb * 8192;
 
   f32x16 dk[4], dv[4];
 #pragma unroll
@@ -360,18 +382,18 @@ __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams 
   const int ld_voff_q1 = (int)(ld_row1 * ql_bytes) + (((lane & 15) ^ swz16(ld_row1)) << 4);
   const int ld_voff_o0 = (int)(ld_row0 * ol_bytes) + (((lane & 15) ^ swz16(ld_row0)) << 4);
   const int ld_voff_o1 = (int)(ld_row1 * ol_bytes) + (((lane & 15) ^ swz16(ld_row1)) << 4);
-  auto issue = [&](int tile, int st) {
+  auto issue = [&](int tile, StageQO& dst) __attribute__((always_inline)) {
     const int q0 = tile * BQ;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(qg + q0 * ql_bytes, q_extent - q0 * ql_bytes);
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(og + q0 * ol_bytes, o_extent - q0 * ol_bytes);
-    load_lds16(rq, &sm.qo[st][0][(w * 2) * 1024], ld_voff_q0);
-    load_lds16(rq, &sm.qo[st][0][(w * 2 + 1) * 1024], ld_voff_q1);
-    load_lds16(ro, &sm.qo[st][1][(w * 2) * 1024], ld_voff_o0);
-    load_lds16(ro, &sm.qo[st][1][(w * 2 + 1) * 1024], ld_voff_o1);
+    load_lds16(rq, &dst.q[(w * 2) * 1024], ld_voff_q0);
+    load_lds16(rq, &dst.q[(w * 2 + 1) * 1024], ld_voff_q1);
+    load_lds16(ro, &dst.o[(w * 2) * 1024], ld_voff_o0);
+    load_lds16(ro, &dst.o[(w * 2 + 1) * 1024], ld_voff_o1);
     const int64_t rem = (int64_t)(p.Lq - q0) * 4;
-    if (w == 0) load_lds4(make_rsrc(lse2_row + q0, rem), &sm.lse2[st][0], lane * 4);
-    if (w == 1) load_lds4(make_rsrc(dlt_row + q0, rem), &sm.dlt[st][0], lane * 4);
-    if (segs && w == 2) load_lds4(make_rsrc(segq_row + q0, rem), &sm.seg[st][0], lane * 4);
+    if (w == 0) load_lds4(make_rsrc(lse2_row + q0, rem), &dst.lse2[0], lane * 4);
+    if (w == 1) load_lds4(make_rsrc(dlt_row + q0, rem), &dst.dlt[0], lane * 4);
+    if (segs && w == 2) load_lds4(make_rsrc(segq_row + q0, rem), &dst.seg[0], lane * 4);
   };
   // Row-major operand (Q, dO, K, V rows; row c32 within its 32-row block, chunk 2*sd + h32): the
   // XOR swizzle leaves bit 0 of an even chunk index alone, so the offset is a per-lane base plus
@@ -387,15 +409,15 @@ __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams 
   // same tile and they move through Q and dO together, so each tile is fetched into L2 once and
   // read there by all of them.
   const int t_last = t_begin + ntiles - 1;
-  if (ntiles > 0) issue(t_last, 0);
-  for (int it = 0; it < ntiles; ++it) {
-    const int st = it & 1;
+  // One tile: stage S holds it, the other stage receives the next one.
+  auto step = [&](auto sc, int it) __attribute__((always_inline)) {
+    StageQO& cur = stage(sc);
     const int q0 = (t_last - it) * BQ;
     wait_vmcnt<0>();
     __syncthreads();
-    if (it + 1 < ntiles) issue(t_last - it - 1, st ^ 1);
-    const uint8_t* qt = sm.qo[st][0] + qh * 8192;  // this wave's 32 queries
-    const uint8_t* ot = sm.qo[st][1] + qh * 8192;
+    if (it + 1 < ntiles) issue(t_last - it - 1, stage(StageC<1 - decltype(sc)::value>{}));
+    const uint8_t* qt = cur.q + qh * 8192;  // this wave's 32 queries
+    const uint8_t* ot = cur.o + qh * 8192;
     const int wq0 = q0 + qh * 32;
     bool active = wave_keys && (wq0 < p.Lq);
     bool need_mask = false;
@@ -404,11 +426,11 @@ __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams 
       need_mask = p.k_offset + wk1 > p.q_offset + wq0;
     }
     if (segs) {
-      const int32_t ts0 = sm.seg[st][qh * 32], ts1 = sm.seg[st][min(qh * 32 + 32, p.Lq - q0) - 1];
+      const int32_t ts0 = cur.seg[qh * 32], ts1 = cur.seg[min(qh * 32 + 32, p.Lq - q0) - 1];
       active = active && !(ts1 < wseg0 || ts0 > wseg1);
       need_mask = need_mask || !(ts0 == ts1 && wseg0 == wseg1 && ts0 == wseg0);
     }
-    if (!active) continue;
+    if (!active) return;
 
     // S = Q K^T and dP = dO V^T (32 queries x 32 keys); the four operand fragments of feature
     // step sd + 1 are read while the two MFMAs of step sd run
@@ -438,8 +460,8 @@ __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams 
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int r4 = qh * 32 + 8 * g + 4 * h32;
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse2[st][r4]);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dlt[st][r4]);
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&cur.lse2[r4]);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&cur.dlt[r4]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int i = 4 * g + j;
@@ -453,7 +475,7 @@ __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams 
       int lo = -BQ;
       if (p.causal) lo = (int)imax64(-BQ, imin64(BQ, gk - p.q_offset - q0));
       lo -= qh * 32 + 4 * h32;
-      const int32_t* segt = &sm.seg[st][qh * 32 + 4 * h32];
+      const int32_t* segt = &cur.seg[qh * 32 + 4 * h32];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         i32x4 qs = {myseg, myseg, myseg, myseg};
@@ -491,17 +513,32 @@ __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams 
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+  };
+  if (ntiles > 0) issue(t_last, lds_qo0);
+  int it = 0;
+  for (; it + 2 <= ntiles; it += 2) {
+    step(StageC<0>{}, it);
+    step(StageC<1>{}, it + 1);
   }
+  if (it < ntiles) step(StageC<0>{}, it);
   __syncthreads();
-  // add the second query half's partial sums (waves 4..7) to the first's (waves 0..3) via LDS
-  f32x4* xch = reinterpret_cast<f32x4*>(&sm);  // [key block][tensor][db][16 groups of 4][64 lanes]
+  // add the second query half's partial sums (waves 4..7) to the first's (waves 0..3) via LDS:
+  // dK^T partials in the K/V area [key block][db][16 groups of 4][64 lanes], dV^T partials of
+  // feature block db in the Q (db even) or dO (db odd) area of stage db / 2, [key block][group][lane]
+  auto xdk = [&](int db, int g) __attribute__((always_inline)) {
+    return reinterpret_cast<f32x4*>(lds_kv) + ((kb * 4 + db) * 4 + g) * 64 + lane;
+  };
+  auto xdv = [&](int db, int g) __attribute__((always_inline)) {
+    uint8_t* area = db == 0 ? lds_qo0.q : db == 1 ? lds_qo0.o : db == 2 ? lds_qo1.q : lds_qo1.o;
+    return reinterpret_cast<f32x4*>(area) + (kb * 4 + g) * 64 + lane;
+  };
   if (qh == 1) {
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        xch[(((kb * 2 + 0) * 4 + db) * 4 + g) * 64 + lane] = f32x4{dk[db][4 * g], dk[db][4 * g + 1], dk[db][4 * g + 2], dk[db][4 * g + 3]};
-        xch[(((kb * 2 + 1) * 4 + db) * 4 + g) * 64 + lane] = f32x4{dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]};
+        *xdk(db, g) = f32x4{dk[db][4 * g], dk[db][4 * g + 1], dk[db][4 * g + 2], dk[db][4 * g + 3]};
+        *xdv(db, g) = f32x4{dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]};
       }
   }
   __syncthreads();
@@ -510,8 +547,8 @@ __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams 
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const f32x4 a = xch[(((kb * 2 + 0) * 4 + db) * 4 + g) * 64 + lane];
-        const f32x4 c = xch[(((kb * 2 + 1) * 4 + db) * 4 + g) * 64 + lane];
+        const f32x4 a = *xdk(db, g);
+        const f32x4 c = *xdv(db, g);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           dk[db][4 * g + j] += a[j];
@@ -522,8 +559,10 @@ __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams 
   __syncthreads();
   // waves 0..3 store (the row helpers have block-wide barriers: every wave takes part)
   const int rows_valid = qh == 0 ? max(0, min(32, p.Lk - wk0)) : 0;
+  // staging rows (16 KB per wave): waves 0..3 in the K/V area, 4..7 in the stages' Q / dO areas
+  uint8_t* const stage_w = w < 4 ? lds_kv + w * (32 * D * 4)
+                                 : (w == 4 ? lds_qo0.q : w == 5 ? lds_qo0.o : w == 6 ? lds_qo1.q : lds_qo1.o);
   if (p.dk_acc) {  // backward ring step: dK, dV += this query block's share, in float32
-    uint8_t* stage_w = reinterpret_cast<uint8_t*>(&sm) + w * (32 * D * 4);
     add_rows_f32(stage_w, dk, p.scale, p.dk_acc + b * p.sdka.b + hh * p.sdka.h + wk0 * p.sdka.l, p.sdka.l, rows_valid);
     add_rows_f32(stage_w, dv, 1.f, p.dv_acc + b * p.sdva.b + hh * p.sdva.h + wk0 * p.sdva.l, p.sdva.l, rows_valid);
   } else {
@@ -533,7 +572,6 @@ __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams 
                                             p.rope.k_pos_offset);
       rope_unrotate_acc(dk, pos, p.rope, h32);
     }
-    uint8_t* stage_w = reinterpret_cast<uint8_t*>(&sm) + w * (32 * D * 2);
     store_rows_bf16(stage_w, dk, p.scale, p.dk + b * p.sdk.b + hh * p.sdk.h + wk0 * p.sdk.l, p.sdk.l, rows_valid);
     store_rows_bf16(stage_w, dv, 1.f, p.dv + b * p.sdv.b + hh * p.sdv.h + wk0 * p.sdv.l, p.sdv.l, rows_valid);
   }
