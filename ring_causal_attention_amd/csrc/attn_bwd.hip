@@ -271,8 +271,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
 // ------------------------------------------------------------------------------ dK / dV
 // A workgroup owns 128 keys and has 8 waves, two per SIMD: wave w handles the 32 keys
 // k0 + 32 (w % 4) against the query half w / 4 of every 64-query tile, so each wave keeps one
-// 32-key dK^T and dV^T accumulator pair (128 registers) and the SIMD's two waves overlap one's
-// MFMAs with the other's softmax.  The two partial sums of a key block are added through LDS at
+// 32-key dK^T and dV^T accumulator pair (128 registers) and the SIMD's two waves cover each
+// other's LDS and dependency waits.  The two partial sums of a key block are added through LDS at
 // the end.  The workgroup's K and V tiles sit in LDS for the whole pass.
 constexpr int BQ = 64;   // queries per tile
 constexpr int kDkdvWaves = 8;
