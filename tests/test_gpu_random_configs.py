@@ -1,0 +1,66 @@
+"""Seeded random configurations of the forward and backward against the oracle.
+
+Each case draws batch, heads, both lengths (ragged, 1 to 700), both global offsets, causal or not,
+and packed segment ids (sorted, a few to a dozen segments; the query and key sides drawn separately
+when their lengths differ) from one fixed seed, so the set is the same on every run and a failure
+names its case.  The fixed-shape tests cover the edges one at a time; these mix them."""
+import numpy as np
+import pytest
+
+from tests.gpu_utils import need_gpu
+from tests.test_gpu_bwd import bwd_case
+from tests.test_gpu_fwd import run_case
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 48
+
+
+def draw_cases(seed=20261203, n=N_CASES):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        B = int(rng.integers(1, 3))
+        H = int(rng.integers(1, 4))
+        Lq = int(rng.integers(1, 701))
+        Lk = Lq if rng.random() < 0.5 else int(rng.integers(1, 701))
+        causal = bool(rng.random() < 0.75)
+        q_offset = int(rng.integers(0, 601)) if rng.random() < 0.5 else 0
+        k_offset = int(rng.integers(0, 601)) if rng.random() < 0.5 else 0
+        seg = None
+        if rng.random() < 0.5:
+            nseg = int(rng.integers(1, 13))
+            sq = np.sort(rng.integers(0, nseg, size=(B, Lq)), axis=1).astype(np.int32)
+            sk = sq.copy() if Lk == Lq else np.sort(rng.integers(0, nseg, size=(B, Lk)), axis=1).astype(np.int32)
+            seg = (sq, sk)
+        cases.append(dict(B=B, H=H, Lq=Lq, Lk=Lk, causal=causal, q_offset=q_offset, k_offset=k_offset, seg=seg,
+                          seed=5000 + i))
+    return cases
+
+
+CASES = draw_cases()
+
+
+def case_id(c):
+    return (f"B{c['B']}H{c['H']}q{c['Lq']}k{c['Lk']}{'c' if c['causal'] else 'n'}"
+            f"o{c['q_offset']}-{c['k_offset']}{'s' if c['seg'] is not None else ''}")
+
+
+@pytest.mark.parametrize("c", CASES, ids=[case_id(c) for c in CASES])
+def test_forward_random_config(c):
+    need_gpu()
+    run_case("bf16", c["B"], c["Lq"], c["Lk"], c["H"], c["seed"], c["seg"], c["q_offset"], c["k_offset"],
+             c["causal"])
+
+
+@pytest.mark.parametrize("c", CASES[:16], ids=[case_id(c) for c in CASES[:16]])
+def test_forward_fp32_random_config(c):
+    need_gpu()
+    run_case("fp32", c["B"], c["Lq"], c["Lk"], c["H"], c["seed"], c["seg"], c["q_offset"], c["k_offset"],
+             c["causal"])
+
+
+@pytest.mark.parametrize("c", CASES, ids=[case_id(c) for c in CASES])
+def test_backward_random_config(c):
+    need_gpu()
+    bwd_case(c["B"], c["Lq"], c["Lk"], c["H"], c["seed"], c["seg"], c["q_offset"], c["k_offset"], c["causal"])
