@@ -64,3 +64,61 @@ def test_forward_fp32_random_config(c):
 def test_backward_random_config(c):
     need_gpu()
     bwd_case(c["B"], c["Lq"], c["Lk"], c["H"], c["seed"], c["seg"], c["q_offset"], c["k_offset"], c["causal"])
+
+
+def draw_fused_cases(seed=20261204, n=16):
+    """RoPE inside the calls: theta, pair layout, positions restarting per segment, position offsets."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        B, H, L = int(rng.integers(1, 3)), int(rng.integers(1, 4)), int(rng.integers(1, 501))
+        seg = None
+        if rng.random() < 0.5:
+            nseg = int(rng.integers(1, 9))
+            seg = np.sort(rng.integers(0, nseg, size=(B, L)), axis=1).astype(np.int32)
+        cases.append(dict(B=B, H=H, L=L, seg=seg, restart=bool(seg is not None and rng.random() < 0.6),
+                          theta=float(rng.choice([1e4, 1e6, 5e7])),
+                          layout=str(rng.choice(["half", "interleaved"])),
+                          causal=bool(rng.random() < 0.8),
+                          q_offset=int(rng.integers(0, 300)) if rng.random() < 0.4 else 0,
+                          k_offset=int(rng.integers(0, 300)) if rng.random() < 0.4 else 0,
+                          qpo=int(rng.integers(0, 1 << 20)) if rng.random() < 0.5 else 0,
+                          kpo=int(rng.integers(0, 1 << 20)) if rng.random() < 0.5 else 0,
+                          seed=6000 + i))
+    return cases
+
+
+FUSED = draw_fused_cases()
+
+
+@pytest.mark.parametrize("c", FUSED, ids=[f"B{c['B']}H{c['H']}L{c['L']}{c['layout'][0]}{'r' if c['restart'] else ''}"
+                                          f"{'s' if c['seg'] is not None else ''}" for c in FUSED])
+def test_fused_rope_random_config(c):
+    need_gpu()
+    from tests.test_gpu_rope_fused import fused_case
+    fused_case(c["B"], c["L"], c["L"], c["H"], c["seed"], c["theta"], c["layout"], c["seg"], c["restart"],
+               c["q_offset"], c["k_offset"], c["qpo"], c["kpo"], c["causal"])
+
+
+def draw_ring_cases(seed=20261205, n=12):
+    """Backward ring: shard count and size, query block length and global offset, packing."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        n_shards, shard = int(rng.integers(2, 9)), int(rng.integers(1, 301))
+        Lq = int(rng.integers(1, 301))
+        q_off = int(rng.integers(0, n_shards * shard + 1))
+        cases.append(dict(n_shards=n_shards, shard=shard, Lq=Lq, q_off=q_off, segs=bool(rng.random() < 0.4),
+                          seed=7000 + i))
+    return cases
+
+
+RING = draw_ring_cases()
+
+
+@pytest.mark.parametrize("c", RING, ids=[f"n{c['n_shards']}x{c['shard']}q{c['Lq']}@{c['q_off']}{'s' if c['segs'] else ''}"
+                                         for c in RING])
+def test_ring_backward_random_config(c):
+    need_gpu()
+    from tests.test_gpu_ring_bwd import ring_bwd_case
+    ring_bwd_case(c["seed"], c["n_shards"], c["shard"], c["Lq"], c["q_off"], segs=c["segs"])
