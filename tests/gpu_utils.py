@@ -45,7 +45,7 @@ def host(t: torch.Tensor) -> np.ndarray:
 
 
 def seg_dev(seg: np.ndarray) -> torch.Tensor:
-    return torch.from_numpy(np.ascontiguousarray(seg, dtype=np.int32)).cuda()
+    return torch.from_numpy(np.array(seg, dtype=np.int32, order="C")).cuda()  # a writable copy
 
 
 def errors(got: np.ndarray, ref: np.ndarray):
