@@ -10,6 +10,10 @@ Run under the profiler (one counter pass per run, e.g. ``--pmc FETCH_SIZE``):
 ``--copy-mib N`` instead runs a plain device-to-device copy of N MiB (torch ``copy_``), whose
 FETCH_SIZE / WRITE_SIZE give the factor that turns the counters into bytes.
 
+``--medians`` times the attention calls of the five workloads (inputs resident in HBM, RoPE applied
+beforehand) with a HIP event pair around each call on the current stream: 3 warm-up calls, then
+the median, minimum and maximum of 20, printed as JSON.
+
 ``--summarize DIR`` reads the ``*_counter_collection.csv`` files under DIR and writes
 ``profiles/traffic_<workload>.json`` (HBM bytes per launch of each kernel, scaled by the copy
 calibration, tagged with the digest of the kernel sources) plus a Markdown table on stdout.
@@ -123,6 +127,75 @@ def summarize(directory: str, workload: str, copy_mib: int):
     return out
 
 
+def medians(n: int = 20, warm: int = 3) -> dict:
+    """Median / min / max milliseconds of n event-timed calls per workload call (see the module doc)."""
+    import statistics
+
+    import torch
+
+    from . import lwm, path, workloads
+    from .configs import WORKLOADS
+
+    def timed(fn):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(n):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        return {"ms": statistics.median(ts), "min_ms": min(ts), "max_ms": max(ts), "calls": n}
+
+    res = {}
+    for name in ("causal_fp32_L1024", "llama7b_fwd_L32768", "packed_L65536", "train_step_L32768"):
+        w = WORKLOADS[name]
+        d = workloads.device_inputs(workloads.host_inputs(w))
+        seg = d["seg"]
+        qr = lwm.lwm_rope_apply(d["q"], seg=seg, theta=w.theta)
+        kr = lwm.lwm_rope_apply(d["k"], seg=seg, theta=w.theta)
+        o = torch.empty_like(qr)
+        lse = torch.empty((w.B, w.H, w.Lq), dtype=torch.float32, device="cuda")
+        r = timed(lambda: lwm.lwm_blockattn_fwd(qr, kr, d["v"], seg, seg, o=o, lse=lse))
+        r["tflops"] = w.fwd_flop() / r["ms"] / 1e9
+        res[name + " lwm_blockattn_fwd"] = r
+        print(f"[medians] {name} forward {r['ms']:.3f} ms", flush=True)
+        if w.backward:
+            ws = torch.empty(lwm.lwm_blockattn_bwd_workspace_size(w.B, w.H, w.Lq, w.Lk, w.D), dtype=torch.uint8,
+                             device="cuda")
+            dq, dk, dv = torch.empty_like(qr), torch.empty_like(kr), torch.empty_like(d["v"])
+            r = timed(lambda: lwm.lwm_blockattn_bwd(qr, kr, d["v"], o, lse, d["do"], seg, seg, dq=dq, dk=dk, dv=dv,
+                                                    workspace=ws))
+            r["tflops"] = w.bwd_flop() / r["ms"] / 1e9
+            res[name + " lwm_blockattn_bwd"] = r
+            print(f"[medians] {name} backward {r['ms']:.3f} ms", flush=True)
+        del d, qr, kr, o, lse
+        torch.cuda.empty_cache()
+    w = WORKLOADS["ring_share_1M"]
+    d = workloads.device_inputs(workloads.host_inputs(w))
+    S = w.Lq
+    qr = lwm.lwm_rope_apply(d["q"], pos_offset=w.q_offset, theta=w.theta)
+    kr = {j: lwm.lwm_rope_apply(x, pos_offset=j * S, theta=w.theta) for j, x in d["k_shards"].items()}
+    o_acc = torch.empty((w.B, S, w.H, w.D), dtype=torch.float32, device="cuda")
+    lse_acc = torch.empty((w.B, w.H, S), dtype=torch.float32, device="cuda")
+    o = torch.empty_like(qr)
+
+    def ring():
+        o_acc.zero_()
+        lse_acc.fill_(float("-inf"))
+        path.ring_forward(qr, kr, d["v_shards"], w.ring_order(), S, w.q_offset, o_acc=o_acc, lse_acc=lse_acc,
+                          o_final=o)
+
+    r = timed(ring)
+    r["tflops"] = w.fwd_flop() / r["ms"] / 1e9
+    res["ring_share_1M path.ring_forward (41 lwm_ring_step)"] = r
+    print(f"[medians] ring_share_1M ring pass {r['ms']:.3f} ms", flush=True)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", default="train_step_L32768")
@@ -131,7 +204,11 @@ def main():
     ap.add_argument("--summarize", default=None)
     ap.add_argument("--write", action="store_true", help="write profiles/traffic_<workload>.json")
     ap.add_argument("--ring-backward", action="store_true", help="ring workloads: run the backward ring")
+    ap.add_argument("--medians", action="store_true", help="median of 20 timed calls per workload call")
     args = ap.parse_args()
+    if args.medians:
+        print(json.dumps(medians(), indent=1))
+        return
     if args.summarize:
         res = summarize(args.summarize, args.workload, args.copy_mib or 1024)
         if args.write:

@@ -50,5 +50,5 @@ def device_inputs(h: dict, device="cuda") -> dict:
     for name in ("k_shards", "v_shards"):
         if name in h:
             d[name] = {j: to_device(x, w.dtype, device) for j, x in h[name].items()}
-    d["seg"] = None if h["seg"] is None else torch.from_numpy(h["seg"]).to(device)
+    d["seg"] = None if h["seg"] is None else torch.from_numpy(np.array(h["seg"], dtype=np.int32)).to(device)
     return d
