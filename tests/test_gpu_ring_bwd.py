@@ -1,6 +1,15 @@
 """lwm_ring_step_bwd: KV shards visited backward around the ring, each adding its share of the
-gradients, give the gradients of attention over all keys (oracle: the backward ring step summed
-over shards, pinned against autograd through SDPA)."""
+gradients, give the gradients of attention over all keys ("开源巨兽LWM：如何用RingAttention撬动百万Token
+多模态世界", section 3.1: the query block stays while key/value blocks travel the ring).
+
+Three checks per case:
+* end to end: dQ, and dK / dV with the shards concatenated, against the oracle's gradients of
+  attention over all keys, from the exact inputs and the oracle's own O (the definition);
+* the same ring against the library's single-call backward over the concatenated keys, given the
+  same forward results (equal up to float32 summation order and the final bf16 rounding);
+* per shard: each step against the oracle's backward ring step on the O and lse the GPU forward
+  produced (a unit check of one step: the step is a function of that O and lse).
+"""
 import numpy as np
 import pytest
 import torch
@@ -8,13 +17,14 @@ import torch
 import oracle
 from ring_causal_attention_amd import lwm, path, synth
 from tests.gpu_utils import (BF16_MAX_ABS, BF16_MEAN_ABS, GRAD_REL_FRO, dev, errors, exact_host, host, need_gpu, note,
-                             rel_fro, seg_dev)
+                             rel_fro, report, seg_dev)
 
 pytestmark = pytest.mark.gpu
 
 
 def ring_bwd_case(seed, n_shards, shard, Lq, q_off, H=2, segs=False, order=None):
-    """GPU forward + backward ring against the oracle's per-shard contributions."""
+    """GPU forward + backward ring: end to end against the oracle over all keys, against the
+    single-call backward, and step by step against the oracle's backward ring step."""
     Ltot = n_shards * shard
     q = synth.normal(seed, "q", (1, Lq, H, 128))
     do = synth.normal(seed, "do", (1, Lq, H, 128))
@@ -37,14 +47,34 @@ def ring_bwd_case(seed, n_shards, shard, Lq, q_off, H=2, segs=False, order=None)
     torch.cuda.synchronize()
 
     qe, doe, ke, ve = (exact_host(x, "bf16") for x in (q, do, k_all, v_all))
+    seg_k_all = None if seg is None else seg[:, :Ltot]
     # the ring forward against attention over all keys
-    ex_o, _ = oracle.attention_fwd(qe, ke, ve, seg_q, seg, q_off, 0, True)
+    ex_o, _ = oracle.attention_fwd(qe, ke, ve, seg_q, seg_k_all, q_off, 0, True)
     mx, mean = errors(host(o), ex_o)
     assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, ("o", mx, mean)
-    # The backward step is defined on the forward's results: the oracle takes the O (bf16) and lse
-    # that the kernels received.  With the exact O instead, a query that sees few keys turns the
-    # bf16 rounding of O into a larger relative error of dP - delta (a cancellation) in the rows
-    # of the shards it reaches, which is the forward's rounding, not the backward's.
+
+    def concat(acc):  # shards in key order; a shard the ring skipped contributes zeros
+        return np.concatenate([host(acc[j]) if j in acc else np.zeros((1, shard, H, 128)) for j in range(n_shards)],
+                              axis=1)
+
+    got_dq, got_dk, got_dv = host(dq_acc), concat(dk_acc), concat(dv_acc)
+    # (1) end to end: the gradients of attention over all keys (exact inputs, the oracle's own O)
+    ex_dq, ex_dk, ex_dv = oracle.attention_bwd(qe, ke, ve, doe, seg_q, seg_k_all, q_off, 0, True)
+    for name, got, ref in (("dq", got_dq, ex_dq), ("dk", got_dk, ex_dk), ("dv", got_dv, ex_dv)):
+        e = rel_fro(got, ref)
+        assert e <= GRAD_REL_FRO, ("end to end", name, e)
+    # (2) the library's single-call backward over the concatenated keys, same forward results
+    k_cat, v_cat = torch.cat(kd, dim=1), torch.cat(vd, dim=1)
+    sk_cat = None if seg is None else seg_dev(seg_k_all)
+    mdq, mdk, mdv = lwm.lwm_blockattn_bwd(qd, k_cat, v_cat, o, lse, dod, seg_q=sqd, seg_k=sk_cat, q_offset=q_off,
+                                          k_offset=0)
+    torch.cuda.synchronize()
+    for name, got, ref in (("dq", got_dq, host(mdq)), ("dk", got_dk, host(mdk)), ("dv", got_dv, host(mdv))):
+        e = rel_fro(got, ref)
+        assert e <= 5e-3, ("vs single-call backward", name, e)
+    # (3) per shard, on the O (bf16) and lse the GPU forward produced: in a shard that a query
+    # reaches through only a few keys, dP - delta cancels, so the forward's rounding of O weighs
+    # more in that shard's share than in the whole gradient
     ref_o, ref_l = host(o), host(lse)
     ref_dq = np.zeros_like(qe)
     for j in range(n_shards):
@@ -61,8 +91,10 @@ def ring_bwd_case(seed, n_shards, shard, Lq, q_off, H=2, segs=False, order=None)
                     assert not bool(got.any()), (name, j)
         else:
             assert not np.any(dkj) and not np.any(dvj), j  # skipped shards add nothing
-    e = rel_fro(host(dq_acc), ref_dq)
+    e = rel_fro(got_dq, ref_dq)
     assert e <= GRAD_REL_FRO, ("dq", e)
+    report(f"ring_bwd n{n_shards}x{shard} q{Lq}@{q_off}{'s' if segs else ''}", dq_rel_fro=rel_fro(got_dq, ex_dq),
+           dk_rel_fro=rel_fro(got_dk, ex_dk), dv_rel_fro=rel_fro(got_dv, ex_dv))
     return dq_acc, dk_acc, dv_acc
 
 
