@@ -118,11 +118,20 @@ int lwm_blockattn_fwd(const lwm_tensor4* q, const lwm_tensor4* k, const lwm_tens
                       int64_t k_offset, int32_t causal, float scale, const lwm_tensor4* o,
                       float* lse, void* stream);
 
-/* Bytes of workspace lwm_blockattn_bwd needs for these sizes (a multiple of 256). */
+/*
+ * Bytes of workspace lwm_blockattn_bwd (and lwm_ring_step_bwd) needs for these sizes: two float32
+ * rows per query (D_i and lse_i * log2(e)), each array rounded up to 256 bytes; at least 256.
+ * Depends on B, H and Lq only; Lk and D are accepted for symmetry with the call.
+ */
 size_t lwm_blockattn_bwd_workspace_size(int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D);
 
 /*
- * Blockwise attention backward (bf16 only), for the loss sum(dout * O):
+ * Blockwise attention backward (bf16 only).  The pages train the model with RingAttention at
+ * up to a million tokens ("LWM：突破 100 万 Token 的开源大模型", section 概述; the context is grown
+ * step by step during training, "[论文解读] World Model on Million-Length Video And Language With
+ * Blockwise RingAttention", section 提出的方法), so the attention's gradients are part of the
+ * method; they are not written out there.  This is the gradient of the loss sum(dout * O) of
+ * the forward defined above (the textbook backward of softmax attention):
  *     D_i = sum_d dout_id O_id,  P = exp(S - lse),  dV = P^T dout,  dP = dout V^T,
  *     dS = P o (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
  * q, k, v, seg_*, offsets, causal, scale as in lwm_blockattn_fwd; o and lse are that call's
@@ -130,7 +139,10 @@ size_t lwm_blockattn_bwd_workspace_size(int64_t B, int64_t H, int64_t Lq, int64_
  * (not accumulated) and are gradients w.r.t. the operands given (the rotated Q', K'); apply
  * lwm_rope_apply(inverse=1) to dq and dk for gradients w.r.t. the pre-RoPE Q and K.
  * workspace: device memory of at least lwm_blockattn_bwd_workspace_size() bytes, 256-byte
- * aligned; its contents on entry do not matter.
+ * aligned; its contents on entry do not matter.  Status: LWM_ERR_INVALID_ARG for NULL or
+ * misaligned pointers and mismatched shapes, LWM_ERR_UNSUPPORTED for fp32 operands, D != 128 or
+ * launch grids beyond 2^31 - 1 workgroups, LWM_ERR_WORKSPACE for a short or misaligned
+ * workspace, LWM_ERR_HIP if a launch fails.
  */
 int lwm_blockattn_bwd(const lwm_tensor4* q, const lwm_tensor4* k, const lwm_tensor4* v,
                       const lwm_tensor4* o, const float* lse, const lwm_tensor4* dout,

@@ -22,7 +22,7 @@ SOURCES = ["abi.cpp", "profile.cpp", "rope.hip", "attn_fwd.hip", "attn_bwd.hip",
 
 # Packed-FP32 VALU forms are disabled for device code; the host pass ignores the feature.
 HIPCC_FLAGS = [
-    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-munsafe-fp-atomics",
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
 ]

@@ -85,7 +85,10 @@ int check_attention(const lwm_tensor4* q, const lwm_tensor4* k, const lwm_tensor
   if (q_offset < 0 || k_offset < 0 || q_offset > (int64_t(1) << 40) || k_offset > (int64_t(1) << 40))
     return fail(LWM_ERR_INVALID_ARG, "offsets must be in [0, 2^40]");
   if (causal != 0 && causal != 1) return fail(LWM_ERR_INVALID_ARG, "causal must be 0 or 1");
-  if ((q->B * q->H) > (int64_t(1) << 31) / ((q->L + 127) / 128 + 1)) return fail(LWM_ERR_UNSUPPORTED, "grid too large");
+  // launch grids: (query tiles or key tiles of 128 rows) x B x H workgroups, each below 2^31
+  const int64_t tiles = ((q->L > k->L ? q->L : k->L) + 127) / 128 + 1;
+  if (q->B * q->H > ((int64_t(1) << 31) - 1) / tiles)
+    return fail(LWM_ERR_UNSUPPORTED, "grid too large: B*H*ceil(max(Lq, Lk)/128) must stay below 2^31");
   return LWM_OK;
 }
 

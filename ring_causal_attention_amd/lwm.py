@@ -98,23 +98,33 @@ def _check(status: int):
         raise LwmError(status, lib().lwm_last_error().decode(errors="replace"))
 
 
-def tensor4(t: torch.Tensor | None) -> Tensor4 | None:
-    """Describe a [B, L, H, D] tensor (feature stride 1) for the ABI."""
+def _on_device(t: torch.Tensor, name: str, device) -> None:
+    """Device memory only, and on the device of the call's first operand: the library takes raw
+    pointers and cannot tell host memory, or another GPU's, from its own."""
+    if not t.is_cuda:
+        raise ValueError(f"{name}: expected a GPU tensor, got one on {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, but the call's tensors are on {device}")
+
+
+def tensor4(t: torch.Tensor | None, name: str = "tensor", device=None) -> Tensor4 | None:
+    """Describe a [B, L, H, D] GPU tensor (feature stride 1) for the ABI."""
     if t is None:
         return None
     if t.dim() != 4:
-        raise ValueError(f"expected a [B, L, H, D] tensor, got shape {tuple(t.shape)}")
+        raise ValueError(f"{name}: expected a [B, L, H, D] tensor, got shape {tuple(t.shape)}")
     if t.dtype == torch.bfloat16:
         dt = LWM_BF16
     elif t.dtype == torch.float32:
         dt = LWM_FP32
     else:
-        raise ValueError(f"unsupported dtype {t.dtype}")
+        raise ValueError(f"{name}: unsupported dtype {t.dtype}")
+    _on_device(t, name, device)
     B, L, H, D = t.shape
     if t.numel() == 0:  # no element is addressed: describe it with contiguous strides
         return Tensor4(t.data_ptr(), dt, 0, B, L, H, D, L * H * D, H * D, D)
     if t.shape[3] > 1 and t.stride(3) != 1:
-        raise ValueError("the feature dimension must be contiguous")
+        raise ValueError(f"{name}: the feature dimension must be contiguous")
     return Tensor4(t.data_ptr(), dt, 0, B, L, H, D, t.stride(0), t.stride(1), t.stride(2))
 
 
@@ -130,12 +140,35 @@ def _stream(t: torch.Tensor):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
-def _seg(s):
+def _seg(s, B, L, device, name="segment ids"):
+    """Segment ids or positions: contiguous int32 [B, L] on the call's device (or None)."""
     if s is None:
         return None
     if s.dtype != torch.int32 or not s.is_contiguous():
-        raise ValueError("segment ids / positions must be contiguous int32 [B, L]")
+        raise ValueError(f"{name}: must be contiguous int32 [B, L]")
+    if tuple(s.shape) != (B, L):
+        raise ValueError(f"{name}: shape {tuple(s.shape)}, expected {(B, L)}")
+    _on_device(s, name, device)
     return s
+
+
+def _rows(t, B, H, L, device, name):
+    """Per-row float32 [B, H, L] (lse, lse_acc): contiguous, on the call's device (or None)."""
+    if t is None:
+        return None
+    if t.dtype != torch.float32 or not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous float32 [B, H, L]")
+    if tuple(t.shape) != (B, H, L):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {(B, H, L)}")
+    _on_device(t, name, device)
+    return t
+
+
+def _workspace(ws, device):
+    if ws.dtype != torch.uint8 or ws.dim() != 1 or not ws.is_contiguous():
+        raise ValueError("workspace: must be a contiguous 1-D uint8 tensor")
+    _on_device(ws, "workspace", device)
+    return ws
 
 
 def lwm_abi_version() -> int:
@@ -145,8 +178,11 @@ def lwm_abi_version() -> int:
 def lwm_rope_apply(x, y=None, pos=None, seg=None, pos_offset=0, theta=10000.0, layout="half", inverse=False):
     """RoPE of x into y (default: a new tensor; pass y=x for in place).  Returns y."""
     y = torch.empty_like(x) if y is None else y
-    _check(lib().lwm_rope_apply(_ref(tensor4(x)), _ref(tensor4(y)), _ptr(_seg(pos)), _ptr(_seg(seg)), int(pos_offset),
-                                float(theta), LAYOUTS[layout], int(bool(inverse)), _stream(x)))
+    B, L = x.shape[0], x.shape[1]
+    dv = x.device
+    _check(lib().lwm_rope_apply(_ref(tensor4(x, "x", dv)), _ref(tensor4(y, "y", dv)), _ptr(_seg(pos, B, L, dv, "pos")),
+                                _ptr(_seg(seg, B, L, dv, "seg")), int(pos_offset), float(theta), LAYOUTS[layout],
+                                int(bool(inverse)), _stream(x)))
     return y
 
 
@@ -157,9 +193,11 @@ def lwm_blockattn_fwd(q, k, v, seg_q=None, seg_k=None, q_offset=0, k_offset=0, c
     o = torch.empty_like(q) if o is None else o
     if lse is None and want_lse:
         lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
-    _check(lib().lwm_blockattn_fwd(_ref(tensor4(q)), _ref(tensor4(k)), _ref(tensor4(v)), _ptr(_seg(seg_q)),
-                                   _ptr(_seg(seg_k)), int(q_offset), int(k_offset), int(bool(causal)), float(scale),
-                                   _ref(tensor4(o)), _ptr(lse), _stream(q)))
+    dv, Lk = q.device, k.shape[1]
+    _check(lib().lwm_blockattn_fwd(_ref(tensor4(q, "q", dv)), _ref(tensor4(k, "k", dv)), _ref(tensor4(v, "v", dv)),
+                                   _ptr(_seg(seg_q, B, Lq, dv, "seg_q")), _ptr(_seg(seg_k, B, Lk, dv, "seg_k")),
+                                   int(q_offset), int(k_offset), int(bool(causal)), float(scale),
+                                   _ref(tensor4(o, "o", dv)), _ptr(_rows(lse, B, H, Lq, dv, "lse")), _stream(q)))
     return o, lse
 
 
@@ -177,11 +215,14 @@ def lwm_blockattn_bwd(q, k, v, o, lse, dout, seg_q=None, seg_k=None, q_offset=0,
     need = lwm_blockattn_bwd_workspace_size(B, H, Lq, k.shape[1], D)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    _check(lib().lwm_blockattn_bwd(_ref(tensor4(q)), _ref(tensor4(k)), _ref(tensor4(v)), _ref(tensor4(o)), _ptr(lse),
-                                   _ref(tensor4(dout)), _ptr(_seg(seg_q)), _ptr(_seg(seg_k)), int(q_offset),
-                                   int(k_offset), int(bool(causal)), float(scale), _ref(tensor4(dq)),
-                                   _ref(tensor4(dk)), _ref(tensor4(dv)), _ptr(workspace),
-                                   workspace.numel() * workspace.element_size(), _stream(q)))
+    d, Lk = q.device, k.shape[1]
+    _check(lib().lwm_blockattn_bwd(_ref(tensor4(q, "q", d)), _ref(tensor4(k, "k", d)), _ref(tensor4(v, "v", d)),
+                                   _ref(tensor4(o, "o", d)), _ptr(_rows(lse, B, H, Lq, d, "lse")),
+                                   _ref(tensor4(dout, "dout", d)), _ptr(_seg(seg_q, B, Lq, d, "seg_q")),
+                                   _ptr(_seg(seg_k, B, Lk, d, "seg_k")), int(q_offset), int(k_offset),
+                                   int(bool(causal)), float(scale), _ref(tensor4(dq, "dq", d)),
+                                   _ref(tensor4(dk, "dk", d)), _ref(tensor4(dv, "dv", d)),
+                                   _ptr(_workspace(workspace, d)), workspace.numel(), _stream(q)))
     return dq, dk, dv
 
 
@@ -202,10 +243,13 @@ def lwm_blockattn_fwd_rope(q, k, v, theta, seg_q=None, seg_k=None, q_offset=0, k
     if q_rot is None and want_q_rot:
         q_rot = torch.empty_like(q)
     ra = rope_args(theta, layout, restart, q_pos_offset, k_pos_offset)
-    _check(lib().lwm_blockattn_fwd_rope(_ref(tensor4(q)), _ref(tensor4(k)), _ref(tensor4(v)), _ptr(_seg(seg_q)),
-                                        _ptr(_seg(seg_k)), int(q_offset), int(k_offset), int(bool(causal)),
-                                        float(scale), ctypes.byref(ra), _ref(tensor4(o)), _ptr(lse),
-                                        _ref(tensor4(q_rot)), _ref(tensor4(k_rot)), _stream(q)))
+    d, Lk = q.device, k.shape[1]
+    _check(lib().lwm_blockattn_fwd_rope(_ref(tensor4(q, "q", d)), _ref(tensor4(k, "k", d)), _ref(tensor4(v, "v", d)),
+                                        _ptr(_seg(seg_q, B, Lq, d, "seg_q")), _ptr(_seg(seg_k, B, Lk, d, "seg_k")),
+                                        int(q_offset), int(k_offset), int(bool(causal)), float(scale),
+                                        ctypes.byref(ra), _ref(tensor4(o, "o", d)),
+                                        _ptr(_rows(lse, B, H, Lq, d, "lse")), _ref(tensor4(q_rot, "q_rot", d)),
+                                        _ref(tensor4(k_rot, "k_rot", d)), _stream(q)))
     return o, lse, q_rot, k_rot
 
 
@@ -221,21 +265,31 @@ def lwm_blockattn_bwd_rope(q_rot, k_rot, v, o, lse, dout, theta, seg_q=None, seg
         workspace = torch.empty(lwm_blockattn_bwd_workspace_size(B, H, Lq, k_rot.shape[1], D), dtype=torch.uint8,
                                 device=q_rot.device)
     ra = rope_args(theta, layout, restart, q_pos_offset, k_pos_offset)
-    _check(lib().lwm_blockattn_bwd_rope(_ref(tensor4(q_rot)), _ref(tensor4(k_rot)), _ref(tensor4(v)),
-                                        _ref(tensor4(o)), _ptr(lse), _ref(tensor4(dout)), _ptr(_seg(seg_q)),
-                                        _ptr(_seg(seg_k)), int(q_offset), int(k_offset), int(bool(causal)),
-                                        float(scale), ctypes.byref(ra), _ref(tensor4(dq)), _ref(tensor4(dk)),
-                                        _ref(tensor4(dv)), _ptr(workspace),
-                                        workspace.numel() * workspace.element_size(), _stream(q_rot)))
+    d, Lk = q_rot.device, k_rot.shape[1]
+    _check(lib().lwm_blockattn_bwd_rope(_ref(tensor4(q_rot, "q_rot", d)), _ref(tensor4(k_rot, "k_rot", d)),
+                                        _ref(tensor4(v, "v", d)), _ref(tensor4(o, "o", d)),
+                                        _ptr(_rows(lse, B, H, Lq, d, "lse")), _ref(tensor4(dout, "dout", d)),
+                                        _ptr(_seg(seg_q, B, Lq, d, "seg_q")), _ptr(_seg(seg_k, B, Lk, d, "seg_k")),
+                                        int(q_offset), int(k_offset), int(bool(causal)), float(scale),
+                                        ctypes.byref(ra), _ref(tensor4(dq, "dq", d)), _ref(tensor4(dk, "dk", d)),
+                                        _ref(tensor4(dv, "dv", d)), _ptr(_workspace(workspace, d)),
+                                        workspace.numel(), _stream(q_rot)))
     return dq, dk, dv
 
 
 def lwm_ring_step(q, k_shard, v_shard, o_acc, lse_acc, seg_q=None, seg_k=None, q_offset=0, k_offset=0,
                   causal=True, scale=0.0, o_final=None):
     """Fold one KV shard into (o_acc float32 [B, Lq, H, D], lse_acc float32 [B, H, Lq]) in place."""
-    _check(lib().lwm_ring_step(_ref(tensor4(q)), _ref(tensor4(k_shard)), _ref(tensor4(v_shard)), _ptr(_seg(seg_q)),
-                               _ptr(_seg(seg_k)), int(q_offset), int(k_offset), int(bool(causal)), float(scale),
-                               _ref(tensor4(o_acc)), _ptr(lse_acc), _ref(tensor4(o_final)), _stream(q)))
+    B, Lq, H, _ = q.shape
+    d, Lk = q.device, k_shard.shape[1]
+    if lse_acc is None:
+        raise ValueError("lse_acc: required")
+    _check(lib().lwm_ring_step(_ref(tensor4(q, "q", d)), _ref(tensor4(k_shard, "k_shard", d)),
+                               _ref(tensor4(v_shard, "v_shard", d)), _ptr(_seg(seg_q, B, Lq, d, "seg_q")),
+                               _ptr(_seg(seg_k, B, Lk, d, "seg_k")), int(q_offset), int(k_offset), int(bool(causal)),
+                               float(scale), _ref(tensor4(o_acc, "o_acc", d)),
+                               _ptr(_rows(lse_acc, B, H, Lq, d, "lse_acc")), _ref(tensor4(o_final, "o_final", d)),
+                               _stream(q)))
     return o_acc, lse_acc
 
 
@@ -247,17 +301,22 @@ def lwm_ring_step_bwd(q, k_shard, v_shard, o, lse, dout, dq_acc, dk_acc, dv_acc,
     need = lwm_blockattn_bwd_workspace_size(B, H, Lq, k_shard.shape[1], D)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    _check(lib().lwm_ring_step_bwd(_ref(tensor4(q)), _ref(tensor4(k_shard)), _ref(tensor4(v_shard)), _ref(tensor4(o)),
-                                   _ptr(lse), _ref(tensor4(dout)), _ptr(_seg(seg_q)), _ptr(_seg(seg_k)), int(q_offset),
-                                   int(k_offset), int(bool(causal)), float(scale), _ref(tensor4(dq_acc)),
-                                   _ref(tensor4(dk_acc)), _ref(tensor4(dv_acc)), _ptr(workspace),
-                                   workspace.numel() * workspace.element_size(), _stream(q)))
+    d, Lk = q.device, k_shard.shape[1]
+    _check(lib().lwm_ring_step_bwd(_ref(tensor4(q, "q", d)), _ref(tensor4(k_shard, "k_shard", d)),
+                                   _ref(tensor4(v_shard, "v_shard", d)), _ref(tensor4(o, "o", d)),
+                                   _ptr(_rows(lse, B, H, Lq, d, "lse")), _ref(tensor4(dout, "dout", d)),
+                                   _ptr(_seg(seg_q, B, Lq, d, "seg_q")), _ptr(_seg(seg_k, B, Lk, d, "seg_k")),
+                                   int(q_offset), int(k_offset), int(bool(causal)), float(scale),
+                                   _ref(tensor4(dq_acc, "dq_acc", d)), _ref(tensor4(dk_acc, "dk_acc", d)),
+                                   _ref(tensor4(dv_acc, "dv_acc", d)), _ptr(_workspace(workspace, d)),
+                                   workspace.numel(), _stream(q)))
     return dq_acc, dk_acc, dv_acc
 
 
-def _matrix(t, name):
+def _matrix(t, name, device=None):
     if t.dtype != torch.bfloat16 or t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
         raise ValueError(f"{name}: expected a bf16 matrix with contiguous rows, got {t.dtype} {tuple(t.shape)}")
+    _on_device(t, name, device)
     return t.stride(0) if t.shape[0] > 1 else t.shape[1]
 
 
@@ -279,10 +338,12 @@ def lwm_blockwise_ffn(x, w_gate, w_up, w_down, chunk=8192, y=None, workspace=Non
     if workspace is None:
         workspace = torch.empty(lwm_blockwise_ffn_workspace_size(rows, d_ff, chunk), dtype=torch.uint8,
                                 device=x.device)
-    _check(lib().lwm_blockwise_ffn(_ptr(x), rows, d_model, _matrix(x, "x"), _ptr(w_gate), _ptr(w_up),
-                                   _matrix(w_gate, "w_gate"), _ptr(w_down), _matrix(w_down, "w_down"), d_ff, _ptr(y),
-                                   _matrix(y, "y"), int(chunk), _ptr(workspace),
-                                   workspace.numel() * workspace.element_size(), _stream(x)))
+    d = x.device
+    _matrix(w_up, "w_up", d)
+    _check(lib().lwm_blockwise_ffn(_ptr(x), rows, d_model, _matrix(x, "x", d), _ptr(w_gate), _ptr(w_up),
+                                   _matrix(w_gate, "w_gate", d), _ptr(w_down), _matrix(w_down, "w_down", d), d_ff,
+                                   _ptr(y), _matrix(y, "y", d), int(chunk), _ptr(_workspace(workspace, d)),
+                                   workspace.numel(), _stream(x)))
     return y
 
 

@@ -199,3 +199,59 @@ def test_ffn_validation():
         assert st == status and needle in msg, (kwargs, st, msg)
     # rows = 0 is a no-op that touches no pointer
     assert call(rows=0, x=None, wg=None, wu=None, wd=None, y=None, ws_ptr=None, nbytes=0)[0] == 0
+
+
+def test_grid_bound_covers_key_tiles():
+    """Launch grids are (query or key tiles of 128) x B x H workgroups: a short query block against a
+    very long key side is refused on the host, like a long query side (no int overflow on device)."""
+    L = _lib()
+    r = ctypes.byref
+    big_h = 65535
+    q = t4(B=65535, L=1, H=big_h, sL=big_h * 128, sB=big_h * 128)
+    k = t4(B=65535, L=1 << 20, H=big_h, sL=big_h * 128, sB=(1 << 20) * big_h * 128)
+    ws = L.lwm_blockattn_bwd_workspace_size(65535, big_h, 1, 1 << 20, 128)
+    st = L.lwm_blockattn_bwd(r(q), r(k), r(k), r(q), 16, r(q), None, None, 0, 0, 1, 0.0, r(q), r(k), r(k), 256, ws,
+                             None)
+    assert st == -2 and "grid too large" in L.lwm_last_error().decode(), L.lwm_last_error()
+    st = L.lwm_blockattn_fwd(r(q), r(k), r(k), None, None, 0, 0, 1, 0.0, r(q), None, None)
+    assert st == -2 and "grid too large" in L.lwm_last_error().decode()
+    # the same sizes with a small batch fit
+    q1 = t4(B=1, L=1, H=2)
+    k1 = t4(B=1, L=1 << 20, H=2)
+    assert L.lwm_blockattn_fwd(r(q1), r(k1), r(k1), None, None, 0, 0, 1, 0.0, r(q1), None, None) != -2 or \
+        "grid" not in L.lwm_last_error().decode()
+
+
+def test_binding_rejects_host_and_misshapen_tensors():
+    """The Python binding refuses CPU tensors and misshapen lse / segment ids / workspace before any
+    call into the library (a raw host pointer would reach the GPU otherwise)."""
+    import torch
+    _lib()
+    q = torch.zeros((1, 8, 2, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        lwm.lwm_blockattn_fwd(q, q, q, o=q.clone(), want_lse=False)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        lwm.lwm_rope_apply(q, theta=1e4)
+    # the argument checks every entry point applies (shape and dtype before the device)
+    dev = torch.device("cuda", 0)
+    with pytest.raises(ValueError, match="lse: shape"):
+        lwm._rows(torch.zeros((1, 2, 7)), 1, 2, 8, dev, "lse")
+    with pytest.raises(ValueError, match="lse: must be contiguous float32"):
+        lwm._rows(torch.zeros((1, 2, 8), dtype=torch.float64), 1, 2, 8, dev, "lse")
+    with pytest.raises(ValueError, match="lse_acc: must be contiguous"):
+        lwm._rows(torch.zeros((1, 8, 2)).transpose(1, 2), 1, 2, 8, dev, "lse_acc")
+    with pytest.raises(ValueError, match="GPU tensor"):
+        lwm._rows(torch.zeros((1, 2, 8)), 1, 2, 8, dev, "lse")
+    with pytest.raises(ValueError, match="seg_k: shape"):
+        lwm._seg(torch.zeros((1, 7), dtype=torch.int32), 1, 8, dev, "seg_k")
+    with pytest.raises(ValueError, match="int32"):
+        lwm._seg(torch.zeros((1, 8), dtype=torch.int64), 1, 8, dev, "seg")
+    with pytest.raises(ValueError, match="GPU tensor"):
+        lwm._seg(torch.zeros((1, 8), dtype=torch.int32), 1, 8, dev, "seg")
+    with pytest.raises(ValueError, match="workspace"):
+        lwm._workspace(torch.zeros(4096, dtype=torch.float32), dev)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        lwm._workspace(torch.zeros(4096, dtype=torch.uint8), dev)
+    with pytest.raises(ValueError, match="x: expected a bf16 matrix"):
+        lwm._matrix(torch.zeros((4, 64)), "x", dev)
+
