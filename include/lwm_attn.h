@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define LWM_ABI_VERSION 4
+#define LWM_ABI_VERSION 5
 
 typedef enum {
   LWM_OK = 0,
@@ -150,6 +150,24 @@ int lwm_blockattn_bwd(const lwm_tensor4* q, const lwm_tensor4* k, const lwm_tens
                       int64_t k_offset, int32_t causal, float scale, const lwm_tensor4* dq,
                       const lwm_tensor4* dk, const lwm_tensor4* dv, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/*
+ * lwm_blockattn_bwd for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same computation and
+ * kernels, with the workspace taken from a static device array the library holds on each GPU
+ * until the process ends (16 MiB: B * H * Lq <= 2^21 query rows).  No workspace argument; every
+ * other argument, result and status as for lwm_blockattn_bwd, plus LWM_ERR_UNSUPPORTED when
+ * B * H * Lq exceeds 2^21.  Allocates nothing (its first call on a device looks up that device's
+ * array address).  The array is shared by every call on one GPU and is fully rewritten before
+ * it is read, so nothing must be cleared between calls; calls that may run concurrently on one
+ * GPU (different streams or threads without ordering) race on it and must be serialised by the
+ * caller.
+ */
+int lwm_blockattn_bwd_noalloc(const lwm_tensor4* q, const lwm_tensor4* k, const lwm_tensor4* v,
+                              const lwm_tensor4* o, const float* lse, const lwm_tensor4* dout,
+                              const int32_t* seg_q, const int32_t* seg_k, int64_t q_offset,
+                              int64_t k_offset, int32_t causal, float scale, const lwm_tensor4* dq,
+                              const lwm_tensor4* dk, const lwm_tensor4* dv, void* stream);
 
 /*
  * One ring step (bf16): fold KV shard (k_shard, v_shard) into the running state of the

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/lwm_attn.h"
 #include "kernels.hpp"
@@ -308,6 +309,58 @@ int lwm_blockattn_bwd(const lwm_tensor4* q, const lwm_tensor4* k, const lwm_tens
   p.dv = static_cast<uint16_t*>(dv->ptr);
   p.sdq = strides(dq); p.sdk = strides(dk); p.sdv = strides(dv);
   return hip_status(lwm::launch_attn_bwd(p, static_cast<hipStream_t>(stream)), "backward launch");
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of lwm_blockattn_bwd_noalloc: a static device array, one copy per GPU, held until the
+// process ends.  It holds the same two float32 rows per query (D_i, lse_i * log2 e) as the
+// caller-owned workspace of lwm_blockattn_bwd, for up to kStaticBwdRows query rows (B * H * Lq).
+constexpr int64_t kStaticBwdRows = int64_t(1) << 21;
+constexpr size_t kStaticBwdBytes = 2 * (size_t)kStaticBwdRows * sizeof(float);
+static __device__ __align__(256) uint8_t scratch[kStaticBwdBytes];
+
+// Device address of `scratch` on each GPU, taken once per device with that device current (in
+// host code the array's name is only a stand-in for the symbol, never a device address).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(LWM_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(LWM_ERR_UNSUPPORTED, "device %d beyond the %d supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return fail(LWM_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return LWM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lwm_blockattn_bwd_noalloc(const lwm_tensor4* q, const lwm_tensor4* k, const lwm_tensor4* v,
+                              const lwm_tensor4* o, const float* lse, const lwm_tensor4* dout,
+                              const int32_t* seg_q, const int32_t* seg_k, int64_t q_offset, int64_t k_offset,
+                              int32_t causal, float scale, const lwm_tensor4* dq, const lwm_tensor4* dk,
+                              const lwm_tensor4* dv, void* stream) {
+  if (q && q->B > 0 && q->H > 0 && q->L > 0 && q->B * q->H > kStaticBwdRows / q->L)
+    return fail(LWM_ERR_UNSUPPORTED, "B*H*Lq = %lld query rows exceed the static workspace's %lld",
+                (long long)(q->B * q->H * q->L), (long long)kStaticBwdRows);
+  void* ws = nullptr;
+  int s;
+  if ((s = static_scratch(&ws))) return s;
+  return lwm_blockattn_bwd(q, k, v, o, lse, dout, seg_q, seg_k, q_offset, k_offset, causal, scale, dq, dk, dv, ws,
+                           kStaticBwdBytes, stream);
 }
 
 int lwm_blockattn_bwd_rope(const lwm_tensor4* q_rot, const lwm_tensor4* k_rot, const lwm_tensor4* v,

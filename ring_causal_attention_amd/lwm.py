@@ -40,7 +40,7 @@ class RopeArgs(ctypes.Structure):
 
 _lib = None
 EXPORTS = ["lwm_abi_version", "lwm_last_error", "lwm_rope_apply", "lwm_blockattn_fwd",
-           "lwm_blockattn_bwd_workspace_size", "lwm_blockattn_bwd", "lwm_blockattn_fwd_rope",
+           "lwm_blockattn_bwd_workspace_size", "lwm_blockattn_bwd", "lwm_blockattn_bwd_noalloc", "lwm_blockattn_fwd_rope",
            "lwm_blockattn_bwd_rope", "lwm_ring_step", "lwm_ring_step_bwd",
            "lwm_blockwise_ffn_workspace_size", "lwm_blockwise_ffn", "lwm_profile_enable", "lwm_profile_reset", "lwm_profile_count", "lwm_profile_get"]
 
@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
     L.lwm_blockattn_bwd_workspace_size.argtypes = [I64, I64, I64, I64, I64]
     L.lwm_blockattn_bwd.restype = ctypes.c_int
     L.lwm_blockattn_bwd.argtypes = [P, P, P, P, VP, P, VP, VP, I64, I64, I32, F32, P, P, P, VP, ctypes.c_size_t, VP]
+    L.lwm_blockattn_bwd_noalloc.restype = ctypes.c_int
+    L.lwm_blockattn_bwd_noalloc.argtypes = [P, P, P, P, VP, P, VP, VP, I64, I64, I32, F32, P, P, P, VP]
     R = ctypes.POINTER(RopeArgs)
     L.lwm_blockattn_fwd_rope.restype = ctypes.c_int
     L.lwm_blockattn_fwd_rope.argtypes = [P, P, P, VP, VP, I64, I64, I32, F32, R, P, VP, P, P, VP]
@@ -223,6 +225,22 @@ def lwm_blockattn_bwd(q, k, v, o, lse, dout, seg_q=None, seg_k=None, q_offset=0,
                                    int(bool(causal)), float(scale), _ref(tensor4(dq, "dq", d)),
                                    _ref(tensor4(dk, "dk", d)), _ref(tensor4(dv, "dv", d)),
                                    _ptr(_workspace(workspace, d)), workspace.numel(), _stream(q)))
+    return dq, dk, dv
+
+
+def lwm_blockattn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, seg_q=None, seg_k=None, q_offset=0, k_offset=0,
+                              causal=True, scale=0.0):
+    """lwm_blockattn_bwd with the library's static per-GPU workspace: the caller passes every
+    output (nothing is allocated here or in the call).  Returns (dq, dk, dv)."""
+    B, Lq, H, D = q.shape
+    d, Lk = q.device, k.shape[1]
+    _check(lib().lwm_blockattn_bwd_noalloc(_ref(tensor4(q, "q", d)), _ref(tensor4(k, "k", d)),
+                                           _ref(tensor4(v, "v", d)), _ref(tensor4(o, "o", d)),
+                                           _ptr(_rows(lse, B, H, Lq, d, "lse")), _ref(tensor4(dout, "dout", d)),
+                                           _ptr(_seg(seg_q, B, Lq, d, "seg_q")), _ptr(_seg(seg_k, B, Lk, d, "seg_k")),
+                                           int(q_offset), int(k_offset), int(bool(causal)), float(scale),
+                                           _ref(tensor4(dq, "dq", d)), _ref(tensor4(dk, "dk", d)),
+                                           _ref(tensor4(dv, "dv", d)), _stream(q)))
     return dq, dk, dv
 
 

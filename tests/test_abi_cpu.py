@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol():
     assert set(names) == set(lwm.EXPORTS), names
     for n in names:
         assert hasattr(L, n), n
-    assert L.lwm_abi_version() == 4
+    assert L.lwm_abi_version() == 5
     assert L.lwm_last_error() == b""
 
 
@@ -255,3 +255,12 @@ def test_binding_rejects_host_and_misshapen_tensors():
     with pytest.raises(ValueError, match="x: expected a bf16 matrix"):
         lwm._matrix(torch.zeros((4, 64)), "x", dev)
 
+
+def test_noalloc_backward_size_limit():
+    """The allocation-free backward refuses B*H*Lq beyond its static workspace on the host."""
+    L = _lib()
+    r = ctypes.byref
+    q = t4(B=1, L=1 << 16, H=33, sL=33 * 128, sB=(1 << 16) * 33 * 128)
+    st = L.lwm_blockattn_bwd_noalloc(r(q), r(q), r(q), r(q), 16, r(q), None, None, 0, 0, 1, 0.0, r(q), r(q), r(q),
+                                     None)
+    assert st == -2 and "static workspace" in L.lwm_last_error().decode()
