@@ -66,11 +66,17 @@ struct Vec<float> {  // fp32: 4 elements per 16 bytes
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void rope_kernel(RopeParams p) {
-  __shared__ float2 cs[kTok][kMaxRopeHalf];  // (cos, sin) per token and pair
+  // (cos, sin) per token and pair.  Pair i is kept at slot (i % P) * (half / P) + i / P, where P is
+  // the number of pairs one 16-byte chunk rotates: the lanes of a wave handle consecutive chunks
+  // c and read pair c * P + j together, which then sit in consecutive slots (no LDS bank aliasing).
+  __shared__ float2 cs[kTok][kMaxRopeHalf];
+  constexpr int N = Vec<T>::N;
   const int b = blockIdx.y;
   const int t0 = blockIdx.x * kTok;
   const int half = p.D / 2;
   const int ntok = min(kTok, p.L - t0);
+  const int P = p.layout == 0 ? N : N / 2;  // pairs per chunk: (i, i + D/2) or (2i, 2i + 1)
+  const int nck = half / P;                 // chunks
 
   // ---- phase 1: angles (double), sin/cos (float) for kTok tokens x D/2 pairs
   for (int e = threadIdx.x; e < ntok * half; e += kThreads) {
@@ -82,12 +88,11 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(RopeParams p) {
     else pos = t;
     float s, c;
     rope_cos_sin(pos + p.pos_offset, p.inv_freq[i], c, s);
-    cs[tt][i] = make_float2(c, p.inverse ? -s : s);
+    cs[tt][(i % P) * nck + i / P] = make_float2(c, p.inverse ? -s : s);
   }
   __syncthreads();
 
   // ---- phase 2: rotate every head of the kTok tokens, 16 bytes at a time
-  constexpr int N = Vec<T>::N;
   const T* __restrict__ x = static_cast<const T*>(p.x);
   T* __restrict__ y = static_cast<T*>(p.y);
   if (p.layout == 0) {
@@ -106,7 +111,7 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(RopeParams p) {
       Vec<T>::load(xs + half, bb);
 #pragma unroll
       for (int j = 0; j < N; ++j) {
-        const float2 r = cs[tt][c * N + j];
+        const float2 r = cs[tt][j * nck + c];
         rope_rotate(a[j], bb[j], r.x, r.y, a[j], bb[j]);
       }
       Vec<T>::store(ys, a);
@@ -127,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(RopeParams p) {
       Vec<T>::load(xs, a);
 #pragma unroll
       for (int j = 0; j < N / 2; ++j) {
-        const float2 r = cs[tt][c * (N / 2) + j];
+        const float2 r = cs[tt][j * nck + c];
         rope_rotate(a[2 * j], a[2 * j + 1], r.x, r.y, a[2 * j], a[2 * j + 1]);
       }
       Vec<T>::store(ys, a);
