@@ -77,38 +77,20 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
   const int c32 = lane & 31, h32 = lane >> 5;
   const int nqt = (p.Lq + BM - 1) / BM;
   int bh, qt;
-  map_block(blockIdx.x, nqt, p.B * p.H, true, bh, qt);
+  const bool segs = p.seg_q != nullptr;
+  map_block(blockIdx.x, nqt, p.B * p.H, true, segs, bh, qt);
   const int b = bh / p.H, hh = bh - b * p.H;
   const int q0 = qt * BM;
   const int qlast = min(q0 + BM, p.Lq) - 1;
-  const bool segs = p.seg_q != nullptr;
 
-  int kbeg = 0, kend = p.Lk;
-  if (p.causal) kend = (int)imax64(0, imin64(kend, p.q_offset + qlast - p.k_offset + 1));
-  if (segs) {
-    int lo, hi;
-    segment_range(p.seg_k + (int64_t)b * p.Lk, p.Lk, p.seg_q[(int64_t)b * p.Lq + q0], p.seg_q[(int64_t)b * p.Lq + qlast],
-                  lo, hi);
-    kbeg = max(kbeg, lo);
-    kend = min(kend, hi);
-  }
-  const int t_begin = kbeg / BN;
-  const int ntiles = (kend > kbeg) ? (kend + BN - 1) / BN - t_begin : 0;
-
+  // the wave's rows first (Q, dO, lse, delta): their loads are in flight during the key-range search
   const int wr0 = q0 + w * MW, wr1 = min(wr0 + MW, p.Lq) - 1;
   const bool wave_rows = wr1 >= wr0;
-  int32_t wseg0 = 0, wseg1 = 0;
-  if (segs && wave_rows) {
-    wseg0 = p.seg_q[(int64_t)b * p.Lq + wr0];
-    wseg1 = p.seg_q[(int64_t)b * p.Lq + wr1];
-  }
   const int qrow = wr0 + c32;
   const int64_t gq = p.q_offset + qrow;
-  const int32_t myseg = segs ? p.seg_q[(int64_t)b * p.Lq + min(qrow, p.Lq - 1)] : 0;
   const int64_t row_at = ((int64_t)b * p.H + hh) * p.Lq + qrow;
   const float lse2 = qrow < p.Lq ? p.lse2[row_at] : INFINITY;
   const float dlt = qrow < p.Lq ? p.delta[row_at] : 0.f;
-
   bf16x8 qreg[8], doreg[8];
   {
     const uint16_t* qg = p.q + b * p.sq.b + hh * p.sq.h + (int64_t)qrow * p.sq.l;
@@ -124,6 +106,28 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
       doreg[s] = as_bf16x8(c);
     }
   }
+
+  int kbeg = 0, kend = p.Lk;
+  if (p.causal) kend = (int)imax64(0, imin64(kend, p.q_offset + qlast - p.k_offset + 1));
+  if (segs) {
+    const int32_t* segk = p.seg_k + (int64_t)b * p.Lk;
+    if (causal_self_segments(p.seg_q, p.seg_k, p.Lq, p.Lk, p.q_offset, p.k_offset, p.causal)) {
+      kbeg = max(kbeg, wave_lower_bound(segk, p.Lk, segk[q0]));  // the causal limit ends the range
+    } else {
+      int lo, hi;
+      segment_range(segk, p.Lk, p.seg_q[(int64_t)b * p.Lq + q0], p.seg_q[(int64_t)b * p.Lq + qlast], lo, hi);
+      kbeg = max(kbeg, lo);
+      kend = min(kend, hi);
+    }
+  }
+  const int t_begin = kbeg / BN;
+  const int ntiles = (kend > kbeg) ? (kend + BN - 1) / BN - t_begin : 0;
+  int32_t wseg0 = 0, wseg1 = 0;
+  if (segs && wave_rows) {
+    wseg0 = p.seg_q[(int64_t)b * p.Lq + wr0];
+    wseg1 = p.seg_q[(int64_t)b * p.Lq + wr1];
+  }
+  const int32_t myseg = segs ? p.seg_q[(int64_t)b * p.Lq + min(qrow, p.Lq - 1)] : 0;
   f32x16 acc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
@@ -314,37 +318,14 @@ __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams 
   const int kb = w & 3, qh = w >> 2;  // key block of 32, query half of each 64-query tile
   const int nkt = (p.Lk + BK - 1) / BK;
   int bh, kt;
-  map_block(blockIdx.x, nkt, p.B * p.H, false, bh, kt);
+  const bool segs = p.seg_q != nullptr;
+  map_block(blockIdx.x, nkt, p.B * p.H, false, segs, bh, kt);
   const int b = bh / p.H, hh = bh - b * p.H;
   const int k0 = kt * BK;
   const int klast = min(k0 + BK, p.Lk) - 1;
-  const bool segs = p.seg_q != nullptr;
 
-  // queries that can see any key of this tile
-  int qbeg = 0, qend = p.Lq;
-  if (p.causal) qbeg = (int)imin64(p.Lq, imax64(0, p.k_offset + k0 - p.q_offset));
-  if (segs) {
-    int lo, hi;
-    segment_range(p.seg_q + (int64_t)b * p.Lq, p.Lq, p.seg_k[(int64_t)b * p.Lk + k0], p.seg_k[(int64_t)b * p.Lk + klast],
-                  lo, hi);
-    qbeg = max(qbeg, lo);
-    qend = min(qend, hi);
-  }
-  const int t_begin = qbeg / BQ;
-  const int ntiles = (qend > qbeg) ? (qend + BQ - 1) / BQ - t_begin : 0;
-
-  const int wk0 = k0 + kb * 32, wk1 = min(wk0 + 32, p.Lk) - 1;
-  const bool wave_keys = wk1 >= wk0;
-  int32_t wseg0 = 0, wseg1 = 0;
-  if (segs && wave_keys) {
-    wseg0 = p.seg_k[(int64_t)b * p.Lk + wk0];
-    wseg1 = p.seg_k[(int64_t)b * p.Lk + wk1];
-  }
-  const int krow = wk0 + c32;
-  const int64_t gk = p.k_offset + krow;
-  const int32_t myseg = segs ? p.seg_k[(int64_t)b * p.Lk + min(krow, p.Lk - 1)] : 0;
-
-  // the workgroup's K and V (128 rows each) into LDS: 32 blocks of 1 KB per tensor, 4 per wave
+  // the workgroup's K and V (128 rows each) into LDS: 32 blocks of 1 KB per tensor, 4 per wave;
+  // in flight during the query-range search
   {
     const uint8_t* kgb = reinterpret_cast<const uint8_t*>(p.k + b * p.sk.b + hh * p.sk.h);
     const uint8_t* vgb = reinterpret_cast<const uint8_t*>(p.v + b * p.sv.b + hh * p.sv.h);
@@ -360,6 +341,37 @@ __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams 
       load_lds16(rv, &lds_kv[2 * kTileBytes + blk * 1024], (int)(row * vlb) + c * 16);
     }
   }
+
+  // queries that can see any key of this tile
+  int qbeg = 0, qend = p.Lq;
+  if (p.causal) qbeg = (int)imin64(p.Lq, imax64(0, p.k_offset + k0 - p.q_offset));
+  if (segs) {
+    const int32_t* segq = p.seg_q + (int64_t)b * p.Lq;
+    const int32_t s_last = p.seg_k[(int64_t)b * p.Lk + klast];
+    if (causal_self_segments(p.seg_q, p.seg_k, p.Lq, p.Lk, p.q_offset, p.k_offset, p.causal)) {
+      // the first key's segment starts no later than the key: the causal limit starts the range
+      qend = min(qend, s_last == INT32_MAX ? p.Lq : wave_lower_bound(segq, p.Lq, s_last + 1));
+    } else {
+      int lo, hi;
+      segment_range(segq, p.Lq, p.seg_k[(int64_t)b * p.Lk + k0], s_last, lo, hi);
+      qbeg = max(qbeg, lo);
+      qend = min(qend, hi);
+    }
+  }
+  const int t_begin = qbeg / BQ;
+  const int ntiles = (qend > qbeg) ? (qend + BQ - 1) / BQ - t_begin : 0;
+
+  const int wk0 = k0 + kb * 32, wk1 = min(wk0 + 32, p.Lk) - 1;
+  const bool wave_keys = wk1 >= wk0;
+  int32_t wseg0 = 0, wseg1 = 0;
+  if (segs && wave_keys) {
+    wseg0 = p.seg_k[(int64_t)b * p.Lk + wk0];
+    wseg1 = p.seg_k[(int64_t)b * p.Lk + wk1];
+  }
+  const int krow = wk0 + c32;
+  const int64_t gk = p.k_offset + krow;
+  const int32_t myseg = segs ? p.seg_k[(int64_t)b * p.Lk + min(krow, p.Lk - 1)] : 0;
+
   const uint8_t* kw = lds_kv + kb * 8192;  // this wave's 32 keys
   const uint8_t* vw = lds_kv + 2 * kTileBytes + kb * 8192;
 

@@ -89,18 +89,41 @@ __device__ __forceinline__ void tr_offsets(int lane, int db, int& off_lo, int& o
 // Grid position -> (batch*head, tile).  `descending` numbers tiles from the last one (causal
 // forward: the longest query tiles first); otherwise from the first (backward over keys: the
 // earliest keys have the most queries).  When B*H is a multiple of 8, block ids congruent mod 8
-// (dispatched to the same XCD) walk one head's tiles, so they share that head's L2 working set.
-__device__ __forceinline__ void map_block(int bid, int ntiles, int BH, bool descending, int& bh, int& t) {
+// (dispatched to the same XCD) stay on their own (batch, head) pairs.  Head-major (`tile_major`
+// false): an XCD walks one head's tiles in order, so its resident workgroups share that head's
+// K/V in L2 and, under a causal mask, run longest first.  Tile-major: consecutive block ids take
+// one tile of every (batch, head) before the next tile.  Used for packed rows, where a tile's work
+// is its position inside its segment, not its index: dealing each tile to all heads at once
+// spreads the long tiles of every segment over the launch instead of leaving some for its end.
+__device__ __forceinline__ void map_block(int bid, int ntiles, int BH, bool descending, bool tile_major, int& bh,
+                                          int& t) {
   int slot_t;
   if ((BH & 7) == 0) {
-    const int xcd = bid & 7, slot = bid >> 3;
-    bh = (slot / ntiles) * 8 + xcd;
-    slot_t = slot % ntiles;
+    const int xcd = bid & 7, slot = bid >> 3, per = BH >> 3;
+    if (tile_major) {
+      bh = (slot % per) * 8 + xcd;
+      slot_t = slot / per;
+    } else {
+      bh = (slot / ntiles) * 8 + xcd;
+      slot_t = slot % ntiles;
+    }
+  } else if (tile_major) {
+    bh = bid % BH;
+    slot_t = bid / BH;
   } else {
     bh = bid / ntiles;
     slot_t = bid % ntiles;
   }
   t = descending ? ntiles - 1 - slot_t : slot_t;
+}
+
+// True when the query and key sides share one segment-id array and one global offset under the
+// causal mask (packed self-attention).  Then the segment of a query row reaches at least that row
+// and the segment of a key starts no later than that key, so of each segment range one bound is
+// already implied by the causal limit and only the other needs a search.
+__device__ __forceinline__ bool causal_self_segments(const int32_t* seg_q, const int32_t* seg_k, int Lq, int Lk,
+                                                     int64_t q_offset, int64_t k_offset, int causal) {
+  return causal && seg_q == seg_k && Lq == Lk && q_offset == k_offset;
 }
 
 // Index range [lo, hi) of the rows of `other` (length n_other, segment ids seg_other) that can

@@ -32,7 +32,12 @@
 //    the rotated rows for the backward.  Keys are not rotated here: every query tile streams them
 //    again, and rotating each visit would add a third to the loop's vector work.
 //  * Workgroups are numbered longest-first, and when B*H is a multiple of 8 the (batch, head)
-//    pairs are dealt to the 8 XCDs so the query tiles sharing one head's K/V run on one L2.
+//    pairs are dealt to the 8 XCDs so the query tiles sharing one head's K/V run on one L2.  In a
+//    packed row a tile's work is its position inside its segment, so there each query tile is
+//    dealt to every (batch, head) before the next one (tile-major order).
+//  * When both sides share one segment array and offset under the causal mask (packed
+//    self-attention), one search over the ids gives the key range; the Q rows are loaded first
+//    so that their loads overlap it.
 #include <float.h>
 
 #include <type_traits>
@@ -57,11 +62,17 @@ __device__ inline void key_range(const FwdParams& p, int b, int r0, int r1, int&
     kend = (int)imax64(0, imin64(kend, lim));
   }
   if (p.seg_q) {
-    int lo, hi;
-    segment_range(p.seg_k + (int64_t)b * p.Lk, p.Lk, p.seg_q[(int64_t)b * p.Lq + r0], p.seg_q[(int64_t)b * p.Lq + r1],
-                  lo, hi);
-    kbeg = max(kbeg, lo);
-    kend = min(kend, hi);
+    const int32_t* segk = p.seg_k + (int64_t)b * p.Lk;
+    if (causal_self_segments(p.seg_q, p.seg_k, p.Lq, p.Lk, p.q_offset, p.k_offset, p.causal)) {
+      // one array and offset for both sides: the last row's segment reaches at least the row
+      // itself, so the causal limit already ends the range
+      kbeg = max(kbeg, wave_lower_bound(segk, p.Lk, segk[r0]));
+    } else {
+      int lo, hi;
+      segment_range(segk, p.Lk, p.seg_q[(int64_t)b * p.Lq + r0], p.seg_q[(int64_t)b * p.Lq + r1], lo, hi);
+      kbeg = max(kbeg, lo);
+      kend = min(kend, hi);
+    }
   }
 }
 
@@ -93,35 +104,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdParams p)
   const int c32 = lane & 31, h32 = lane >> 5;
   const int nqt = (p.Lq + BM - 1) / BM;
   int bh, qt;
-  map_block(blockIdx.x, nqt, p.B * p.H, true, bh, qt);
+  map_block(blockIdx.x, nqt, p.B * p.H, true, kSegs, bh, qt);
   const int b = bh / p.H, hh = bh - b * p.H;
   const int q0 = qt * BM;
   const int qlast = min(q0 + BM, p.Lq) - 1;
-
-  int kbeg, kend;
-  key_range(p, b, q0, qlast, kbeg, kend);
-  const int t_begin = kbeg / BN;
-  const int ntiles = (kend > kbeg) ? (kend + BN - 1) / BN - t_begin : 0;
-
   const int wr0 = q0 + w * 32;
   const int wr1 = min(wr0 + 32, p.Lq) - 1;  // may be < wr0 for a ragged last tile
   const bool wave_rows = wr1 >= wr0;
-  int32_t wseg0 = 0, wseg1 = 0;
-  if (kSegs && wave_rows) {
-    wseg0 = p.seg_q[(int64_t)b * p.Lq + wr0];
-    wseg1 = p.seg_q[(int64_t)b * p.Lq + wr1];
-  }
 
+  // the wave's Q rows first: their loads are in flight during the key-range search
   const uint16_t* __restrict__ qg = static_cast<const uint16_t*>(p.q) + b * p.sq.b + hh * p.sq.h;
-  const uint8_t* kg = reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(p.k) + b * p.sk.b + hh * p.sk.h);
-  const uint8_t* vg = reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(p.v) + b * p.sv.b + hh * p.sv.h);
-  const int64_t kl_bytes = p.sk.l * 2, vl_bytes = p.sv.l * 2;
-  const int64_t k_extent = (int64_t)(p.Lk - 1) * kl_bytes + 256, v_extent = (int64_t)(p.Lk - 1) * vl_bytes + 256;
-  const int32_t* segk_row = kSegs ? p.seg_k + (int64_t)b * p.Lk : nullptr;
-
   const int qrow = wr0 + c32;
   const int64_t gq = p.q_offset + qrow;
-  const int32_t myseg = kSegs ? p.seg_q[(int64_t)b * p.Lq + min(qrow, p.Lq - 1)] : 0;
   bf16x8 qreg[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
@@ -129,6 +123,24 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdParams p)
     if (qrow < p.Lq) v = *reinterpret_cast<const u32x4*>(qg + qrow * p.sq.l + s * 16 + h32 * 8);
     qreg[s] = as_bf16x8(v);
   }
+
+  int kbeg, kend;
+  key_range(p, b, q0, qlast, kbeg, kend);
+  const int t_begin = kbeg / BN;
+  const int ntiles = (kend > kbeg) ? (kend + BN - 1) / BN - t_begin : 0;
+
+  int32_t wseg0 = 0, wseg1 = 0;
+  if (kSegs && wave_rows) {
+    wseg0 = p.seg_q[(int64_t)b * p.Lq + wr0];
+    wseg1 = p.seg_q[(int64_t)b * p.Lq + wr1];
+  }
+
+  const uint8_t* kg = reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(p.k) + b * p.sk.b + hh * p.sk.h);
+  const uint8_t* vg = reinterpret_cast<const uint8_t*>(static_cast<const uint16_t*>(p.v) + b * p.sv.b + hh * p.sv.h);
+  const int64_t kl_bytes = p.sk.l * 2, vl_bytes = p.sv.l * 2;
+  const int64_t k_extent = (int64_t)(p.Lk - 1) * kl_bytes + 256, v_extent = (int64_t)(p.Lk - 1) * vl_bytes + 256;
+  const int32_t* segk_row = kSegs ? p.seg_k + (int64_t)b * p.Lk : nullptr;
+  const int32_t myseg = kSegs ? p.seg_q[(int64_t)b * p.Lq + min(qrow, p.Lq - 1)] : 0;
   if constexpr (kRope) {
     // q holds the pre-RoPE rows: rotate them here (the standalone RoPE kernel's arithmetic, so
     // the bits equal those of a separate RoPE pass) and hand the rotated rows on if asked
@@ -424,7 +436,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_f32_kernel(FwdParams p) 
   const int c32 = lane & 31, h32 = lane >> 5;
   const int nqt = (p.Lq + BM - 1) / BM;
   int bh, qt;
-  map_block(blockIdx.x, nqt, p.B * p.H, true, bh, qt);
+  map_block(blockIdx.x, nqt, p.B * p.H, true, p.seg_q != nullptr, bh, qt);
   const int b = bh / p.H, hh = bh - b * p.H;
   const int q0 = qt * BM;
   const int qlast = min(q0 + BM, p.Lq) - 1;

@@ -78,9 +78,11 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(RopeParams p) {
   const int P = p.layout == 0 ? N : N / 2;  // pairs per chunk: (i, i + D/2) or (2i, 2i + 1)
   const int nck = half / P;                 // chunks
 
-  // ---- phase 1: angles (double), sin/cos (float) for kTok tokens x D/2 pairs
+  // ---- phase 1: angles (double), sin/cos (float) for kTok tokens x D/2 pairs; consecutive lanes
+  // fill consecutive slots
   for (int e = threadIdx.x; e < ntok * half; e += kThreads) {
-    const int tt = e / half, i = e - tt * half;
+    const int tt = e / half, slot = e - tt * half;
+    const int i = (slot % nck) * P + slot / nck;  // the pair kept at this slot
     const int t = t0 + tt;
     int64_t pos;
     if (p.pos) pos = p.pos[(int64_t)b * p.L + t];
@@ -88,7 +90,7 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(RopeParams p) {
     else pos = t;
     float s, c;
     rope_cos_sin(pos + p.pos_offset, p.inv_freq[i], c, s);
-    cs[tt][(i % P) * nck + i / P] = make_float2(c, p.inverse ? -s : s);
+    cs[tt][slot] = make_float2(c, p.inverse ? -s : s);
   }
   __syncthreads();
 

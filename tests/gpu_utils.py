@@ -48,6 +48,18 @@ def seg_dev(seg: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.array(seg, dtype=np.int32, order="C")).cuda()  # a writable copy
 
 
+def seg_pair_dev(sq, sk, seed):
+    """Device segment ids for the two sides.  When both are the same ids, even seeds pass one
+    tensor for both (the library's one-array path for packed self-attention), odd seeds two
+    copies (its general path)."""
+    if sq is None:
+        return None, None
+    if seed % 2 == 0 and sq.shape == sk.shape and np.array_equal(sq, sk):
+        d = seg_dev(sq)
+        return d, d
+    return seg_dev(sq), seg_dev(sk)
+
+
 def errors(got: np.ndarray, ref: np.ndarray):
     d = np.abs(got - ref)
     return float(d.max()) if d.size else 0.0, float(d.mean()) if d.size else 0.0

@@ -5,7 +5,7 @@ import torch
 
 import oracle
 from ring_causal_attention_amd import lwm, path, synth
-from tests.gpu_utils import GRAD_REL_FRO, dev, exact_host, host, need_gpu, note, rel_fro, seg_dev
+from tests.gpu_utils import GRAD_REL_FRO, dev, exact_host, host, need_gpu, note, rel_fro, seg_dev, seg_pair_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -18,8 +18,7 @@ def bwd_case(B, Lq, Lk, H, seed, seg=None, q_offset=0, k_offset=0, causal=True):
     if seg is not None:
         sq, sk = seg
     qd, kd, vd, dod = dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), dev(do, "bf16")
-    sqd = None if sq is None else seg_dev(sq)
-    skd = None if sk is None else seg_dev(sk)
+    sqd, skd = seg_pair_dev(sq, sk, seed)
     o, lse = lwm.lwm_blockattn_fwd(qd, kd, vd, sqd, skd, q_offset, k_offset, causal)
     dq, dk, dv = lwm.lwm_blockattn_bwd(qd, kd, vd, o, lse, dod, sqd, skd, q_offset, k_offset, causal)
     torch.cuda.synchronize()

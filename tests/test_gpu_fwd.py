@@ -6,7 +6,7 @@ import torch
 import oracle
 from ring_causal_attention_amd import lwm, synth
 from tests.gpu_utils import (BF16_MAX_ABS, BF16_MEAN_ABS, FP32_MAX_ABS, LSE_BF16, LSE_FP32, dev, errors,
-                             exact_host, host, need_gpu, note, seg_dev)
+                             exact_host, host, need_gpu, note, seg_dev, seg_pair_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -22,9 +22,9 @@ def run_case(dtype, B, Lq, Lk, H, seed, seg=None, q_offset=0, k_offset=0, causal
     sq = sk = None
     if seg is not None:
         sq, sk = seg
-    o, lse = lwm.lwm_blockattn_fwd(dev(q, dtype), dev(k, dtype), dev(v, dtype),
-                                   None if sq is None else seg_dev(sq), None if sk is None else seg_dev(sk),
-                                   q_offset, k_offset, causal, scale)
+    sqd, skd = seg_pair_dev(sq, sk, seed)
+    o, lse = lwm.lwm_blockattn_fwd(dev(q, dtype), dev(k, dtype), dev(v, dtype), sqd, skd, q_offset, k_offset, causal,
+                                   scale)
     torch.cuda.synchronize()
     ro, rl = oracle.attention_fwd(exact_host(q, dtype), exact_host(k, dtype), exact_host(v, dtype), sq, sk,
                                   q_offset, k_offset, causal, None if scale == 0.0 else scale)
