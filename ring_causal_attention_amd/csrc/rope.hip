@@ -3,8 +3,9 @@
 // tensor in place or out of place, forward or inverse.
 //
 // HBM-bound: every element is read and written once.  A workgroup owns kTok consecutive tokens
-// of one batch row.  It first forms the kTok x D/2 angles once (double precision: position times
-// inv_freq, reduced modulo pi/2) and their sine/cosine (rounded to single precision) in LDS, then streams
+// of one batch row.  It finds the kTok positions once (restarting ones by a single segment search
+// per workgroup), forms the kTok x D/2 angles once (double precision: position times inv_freq,
+// reduced modulo pi/2) and their sine/cosine (rounded to single precision) in LDS, then streams
 // all H heads of those tokens with 16-byte vector loads and stores, so the trigonometry is shared
 // by every head instead of being repeated per element.
 #include "kernels.hpp"
@@ -16,17 +17,6 @@ namespace {
 
 constexpr int kTok = 4;
 constexpr int kThreads = 256;
-
-// Index of the first token of t's segment: first p with seg[p] == seg[t], ids non-decreasing.
-__device__ int segment_start(const int32_t* __restrict__ seg, int t) {
-  const int32_t v = seg[t];
-  int lo = 0, hi = t;  // answer in [lo, hi]
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (seg[mid] < v) lo = mid + 1; else hi = mid;
-  }
-  return lo;
-}
 
 template <typename T>
 struct Vec;
@@ -78,18 +68,38 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(RopeParams p) {
   const int P = p.layout == 0 ? N : N / 2;  // pairs per chunk: (i, i + D/2) or (2i, 2i + 1)
   const int nck = half / P;                 // chunks
 
+  // ---- phase 0: the kTok tokens' positions, once per workgroup.  With restarting positions the
+  // first token's segment start comes from one wave-wide search; a later token's segment starts
+  // at the last id change at or before it, else at the first token's start.
+  __shared__ int64_t tpos[kTok];
+  if (threadIdx.x < kWave) {
+    int first0 = 0;
+    const int32_t* srow = p.seg ? p.seg + (int64_t)b * p.L : nullptr;
+    if (!p.pos && srow) first0 = wave_lower_bound(srow, t0 + 1, srow[t0]);
+    const int tt = threadIdx.x;
+    if (tt < ntok) {
+      const int t = t0 + tt;
+      int64_t pos = t;
+      if (p.pos) {
+        pos = p.pos[(int64_t)b * p.L + t];
+      } else if (srow) {
+        int start = first0;
+        for (int u = 1; u <= tt; ++u)
+          if (srow[t0 + u] != srow[t0 + u - 1]) start = t0 + u;
+        pos = t - start;
+      }
+      tpos[tt] = pos + p.pos_offset;
+    }
+  }
+  __syncthreads();
+
   // ---- phase 1: angles (double), sin/cos (float) for kTok tokens x D/2 pairs; consecutive lanes
   // fill consecutive slots
   for (int e = threadIdx.x; e < ntok * half; e += kThreads) {
     const int tt = e / half, slot = e - tt * half;
     const int i = (slot % nck) * P + slot / nck;  // the pair kept at this slot
-    const int t = t0 + tt;
-    int64_t pos;
-    if (p.pos) pos = p.pos[(int64_t)b * p.L + t];
-    else if (p.seg) pos = t - segment_start(p.seg + (int64_t)b * p.L, t);
-    else pos = t;
     float s, c;
-    rope_cos_sin(pos + p.pos_offset, p.inv_freq[i], c, s);
+    rope_cos_sin(tpos[tt], p.inv_freq[i], c, s);
     cs[tt][slot] = make_float2(c, p.inverse ? -s : s);
   }
   __syncthreads();

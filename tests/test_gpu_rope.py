@@ -71,3 +71,18 @@ def test_rope_round_trip_at_one_million():
     y = lwm.lwm_rope_apply(xd, pos_offset=1_048_000, theta=5.0e7)
     z = lwm.lwm_rope_apply(y, pos_offset=1_048_000, theta=5.0e7, inverse=True)
     assert np.max(np.abs(host(z) - x.astype(np.float64))) < 1e-5
+
+
+@pytest.mark.parametrize("layout", ["half", "interleaved"])
+def test_rope_short_segments(layout):
+    """Segments of 1 to 4 tokens, so segment starts fall at every offset inside the groups of
+    tokens a workgroup rotates together, and ids that jump (non-consecutive values)."""
+    need_gpu()
+    B, L, H, D = 2, 203, 2, 128
+    note(f"rope short segments layout={layout}")
+    x = synth.normal(11, "q", (B, L, H, D))
+    seg = synth.random_segment_ids(12, B, L, 4) * 3 + 1
+    y = lwm.lwm_rope_apply(dev(x, "bf16"), theta=1.0e6, layout=layout, seg=seg_dev(seg), pos_offset=2)
+    ref = oracle.rope(exact_host(x, "bf16"), oracle.positions(B, L, 2, seg), 1.0e6, layout)
+    got = host(y)
+    assert np.all(np.abs(got - ref) <= _tol("bf16", ref)), float(np.max(np.abs(got - ref)))
