@@ -16,6 +16,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -67,6 +68,22 @@ def time_steps(step, steps, warmup, lwm, torch):
     lwm.lwm_profile_enable(False)
     prof = lwm.lwm_profile_read()
     return (t1 - t0) * 1e3 / steps, prof
+
+
+def time_settled(step, steps, warmup, lwm, torch, warm_ms=300.0, timed_ms=600.0):
+    """time_steps with the warm-up and the timed steps raised until they cover about warm_ms and
+    timed_ms of work: the extra workloads follow seconds of host-side input generation, after which
+    the GPU clock takes a while under load to settle (a few short steps time it low).  Returns
+    (ms per step, profile, timed steps, warm-up steps)."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    step()
+    torch.cuda.synchronize()
+    one = max((time.perf_counter() - t0) * 1e3, 1e-3)
+    w = max(warmup, math.ceil(warm_ms / one))
+    k = max(steps, math.ceil(timed_ms / one))
+    ms, prof = time_steps(step, k, w, lwm, torch)
+    return ms, prof, k, w
 
 
 def kernels_table(prof, steps):
@@ -141,13 +158,13 @@ def bench_extras(torch, lwm, path, workloads, configs, steps=3, warmup=1):
         lwm.lwm_rope_apply(d["k"], kr, theta=w.theta)
         lwm.lwm_blockattn_fwd(qr, kr, d["v"], o=o, lse=lse)
 
-    ms, prof = time_steps(fwd_step, steps, warmup, lwm, torch)
-    ks = kernels_table(prof, steps)
+    ms, prof, n, nw = time_settled(fwd_step, steps, warmup, lwm, torch)
+    ks = kernels_table(prof, n)
     fk = ks["attn_fwd_bf16"]["avg_ms"]
     out[w.name] = {"ms_per_step": ms, "tflops_with_rope": w.fwd_flop() / ms / 1e9,
                    "attn_fwd_ms": fk, "attn_fwd_tflops": w.fwd_flop() / fk / 1e9,
                    "pct_of_bf16_peak": 100 * w.fwd_flop() / fk / 1e9 / configs.PEAK_BF16_TFLOPS,
-                   "tokens_per_s": w.B * w.Lq / (ms * 1e-3), "kernels": ks}
+                   "tokens_per_s": w.B * w.Lq / (ms * 1e-3), "steps": n, "warmup": nw, "kernels": ks}
     del d, qr, kr, o, lse
     torch.cuda.empty_cache()
 
@@ -162,12 +179,12 @@ def bench_extras(torch, lwm, path, workloads, configs, steps=3, warmup=1):
         lwm.lwm_rope_apply(d["k"], kr, seg=d["seg"], theta=w.theta)
         lwm.lwm_blockattn_fwd(qr, kr, d["v"], d["seg"], d["seg"], o=o, lse=lse)
 
-    ms, prof = time_steps(packed_step, steps, warmup, lwm, torch)
-    ks = kernels_table(prof, steps)
+    ms, prof, n, nw = time_settled(packed_step, steps, warmup, lwm, torch)
+    ks = kernels_table(prof, n)
     fk = ks["attn_fwd_bf16"]["avg_ms"]
     out[w.name] = {"ms_per_step": ms, "attn_fwd_ms": fk, "attn_fwd_tflops": w.fwd_flop() / fk / 1e9,
                    "pct_of_bf16_peak": 100 * w.fwd_flop() / fk / 1e9 / configs.PEAK_BF16_TFLOPS,
-                   "segments": len(w.segment_lengths()), "visible_pairs": w.visible_pairs(), "kernels": ks}
+                   "segments": len(w.segment_lengths()), "visible_pairs": w.visible_pairs(), "steps": n, "warmup": nw, "kernels": ks}
     # the same packed row through a whole training step (forward + backward, segment-aware tile
     # skipping in both backward kernels); dO drawn like the other tensors of the workload
     from ring_causal_attention_amd import synth
@@ -177,14 +194,14 @@ def bench_extras(torch, lwm, path, workloads, configs, steps=3, warmup=1):
     def packed_train_step():
         path.training_step(d["q"], d["k"], d["v"], do, w.theta, seg=d["seg"], buffers=bufs)
 
-    ms, prof = time_steps(packed_train_step, steps, warmup, lwm, torch)
-    ks = kernels_table(prof, steps)
+    ms, prof, n, nw = time_settled(packed_train_step, steps, warmup, lwm, torch)
+    ks = kernels_table(prof, n)
     tflop = 14 * w.D * w.visible_pairs()
     bk = sum(ks[k]["ms_per_step"] for k in ("bwd_delta", "bwd_dq", "bwd_dkdv") if k in ks)
     out[w.name + "_train"] = {"ms_per_step": ms, "tflops": tflop / ms / 1e9,
                               "pct_of_bf16_peak": 100 * tflop / ms / 1e9 / configs.PEAK_BF16_TFLOPS,
                               "attn_bwd_ms": bk, "attn_bwd_tflops": 10 * w.D * w.visible_pairs() / bk / 1e9,
-                              "tokens_per_s": w.B * w.Lq / (ms * 1e-3), "kernels": ks}
+                              "tokens_per_s": w.B * w.Lq / (ms * 1e-3), "steps": n, "warmup": nw, "kernels": ks}
     del d, qr, kr, o, lse, do, bufs
     torch.cuda.empty_cache()
 
@@ -204,15 +221,15 @@ def bench_extras(torch, lwm, path, workloads, configs, steps=3, warmup=1):
         path.ring_forward(qr, kr, d["v_shards"], w.ring_order(), S, w.q_offset, o_acc=o_acc, lse_acc=lse_acc,
                           o_final=o)
 
-    ms, prof = time_steps(ring_step, steps, warmup, lwm, torch)
-    ks = kernels_table(prof, steps)
+    ms, prof, n, nw = time_settled(ring_step, steps, warmup, lwm, torch)
+    ks = kernels_table(prof, n)
     rk = ks["ring_step_bf16"]
     out[w.name] = {"ms_per_step": ms, "ring_steps_per_pass": rk["launches_per_step"],
                    "ring_kernel_ms_per_pass": rk["ms_per_step"],
                    "tflops": w.fwd_flop() / ms / 1e9,
                    "ring_kernel_tflops": w.fwd_flop() / rk["ms_per_step"] / 1e9,
                    "pct_of_bf16_peak": 100 * w.fwd_flop() / rk["ms_per_step"] / 1e9 / configs.PEAK_BF16_TFLOPS,
-                   "query_tokens_per_s": w.B * S / (ms * 1e-3), "kernels": ks}
+                   "query_tokens_per_s": w.B * S / (ms * 1e-3), "steps": n, "warmup": nw, "kernels": ks}
 
     # the same share's backward ring: the 41 shards visit again, each adding its share of the
     # gradients (dQ stays, dK / dV travel with their shard); o / lse_acc hold the forward's result
@@ -228,8 +245,8 @@ def bench_extras(torch, lwm, path, workloads, configs, steps=3, warmup=1):
         path.ring_backward(qr, kr, d["v_shards"], o, lse_acc, d["do"], w.ring_order(), S, w.q_offset,
                            dq_acc=dq_acc, dk_acc=dk_acc, dv_acc=dv_acc, workspace=ws)
 
-    ms, prof = time_steps(ring_bwd_step, steps, warmup, lwm, torch)
-    ks = kernels_table(prof, steps)
+    ms, prof, n, nw = time_settled(ring_bwd_step, steps, warmup, lwm, torch)
+    ks = kernels_table(prof, n)
     kms = sum(ks[k]["ms_per_step"] for k in ("bwd_delta", "bwd_dq", "bwd_dkdv") if k in ks)
     bflop = 10 * w.D * w.visible_pairs()
     out[w.name + "_backward"] = {
@@ -237,7 +254,7 @@ def bench_extras(torch, lwm, path, workloads, configs, steps=3, warmup=1):
         "kernel_ms_per_pass": kms, "tflops": bflop / ms / 1e9, "kernel_tflops": bflop / kms / 1e9,
         "pct_of_bf16_peak": 100 * bflop / kms / 1e9 / configs.PEAK_BF16_TFLOPS,
         "note": "10*D flop per visible pair; ms_per_step also zeroes the float32 accumulators",
-        "kernels": ks}
+        "steps": n, "warmup": nw, "kernels": ks}
     del d, qr, kr, o_acc, lse_acc, o, dq_acc, dk_acc, dv_acc, ws
     torch.cuda.empty_cache()
 
@@ -255,8 +272,8 @@ def bench_extras(torch, lwm, path, workloads, configs, steps=3, warmup=1):
     def ffn_step():
         lwm.lwm_blockwise_ffn(df["x"], df["w_gate"], df["w_up"], df["w_down"], chunk=fw.chunk, y=y, workspace=fws)
 
-    ms, prof = time_steps(ffn_step, steps, warmup, lwm, torch)
-    ks = kernels_table(prof, steps)
+    ms, prof, n, nw = time_settled(ffn_step, steps, warmup, lwm, torch)
+    ks = kernels_table(prof, n)
     per_chunk = 2 * fw.chunk * fw.d_model * fw.d_ff
     traffic = load_traffic(fw) or {}
     roof = {}
@@ -274,20 +291,20 @@ def bench_extras(torch, lwm, path, workloads, configs, steps=3, warmup=1):
             torch.matmul(torch.nn.functional.silu(torch.matmul(xc, wg.t())) * torch.matmul(xc, wu.t()), wd.t(),
                          out=y[r0:r0 + fw.chunk])
 
-    for _ in range(warmup):
+    for _ in range(nw):
         torch_step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(steps):
+    for _ in range(n):
         torch_step()
     torch.cuda.synchronize()
-    torch_ms = (time.perf_counter() - t0) * 1e3 / steps
+    torch_ms = (time.perf_counter() - t0) * 1e3 / n
     out[fw.name] = {"ms_per_step": ms, "tflops": fw.flop() / ms / 1e9,
                     "pct_of_bf16_peak": 100 * fw.flop() / ms / 1e9 / configs.PEAK_BF16_TFLOPS,
                     "tokens_per_s": fw.rows / (ms * 1e-3), "roofline": roof,
                     "torch_matmul_ms_per_step": torch_ms,
                     "note": "6*rows*d_model*d_ff flop; torch_matmul_ms_per_step runs the same three products "
-                            "through torch.matmul and silu for comparison", "kernels": ks}
+                            "through torch.matmul and silu for comparison", "steps": n, "warmup": nw, "kernels": ks}
     del df, y, fws
     torch.cuda.empty_cache()
     return out
