@@ -65,6 +65,15 @@ def test_noncausal_and_heads():
     bwd_case(2, 160, 160, 4, 2302)  # B*H multiple of 8
 
 
+@pytest.mark.parametrize("seed", [2311, 2312])
+def test_packed_heads_multiple_of_eight(seed):
+    """Packed rows with B*H a multiple of 8 (tile-major, XCD-grouped block order in both kernels)."""
+    need_gpu()
+    L = 523
+    seg = synth.random_segment_ids(seed, 1, L, 160)
+    bwd_case(1, L, L, 8, seed, seg=(seg, seg))
+
+
 def test_bwd_deterministic():
     need_gpu()
     note("bwd bitwise determinism")

@@ -81,6 +81,17 @@ def test_custom_scale_and_batch_heads():
     run_case("bf16", 2, 129, 129, 8, 502)  # B*H multiple of 8: XCD-grouped block order
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("seed", [511, 512])
+def test_packed_heads_multiple_of_eight(dtype, seed):
+    """Packed rows with B*H a multiple of 8: tile-major, XCD-grouped block order; the even seed
+    passes one id tensor for both sides (the single-search path), the odd one two equal copies."""
+    need_gpu()
+    L = 611
+    seg = synth.random_segment_ids(seed, 2, L, 140)
+    run_case(dtype, 2, L, L, 4, seed, seg=(seg, seg))
+
+
 def test_rows_with_no_visible_key():
     need_gpu()
     go, gl = run_case("bf16", 1, 100, 100, 2, 601, q_offset=0, k_offset=50)

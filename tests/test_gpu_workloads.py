@@ -30,7 +30,7 @@ def exact(x, dtype):
 
 
 def host_threads() -> int:
-    """Host cores this process may use (at most 16: the share a GPU machine gives one GPU)."""
+    """Host cores this process may use, capped at 16 worker threads."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
