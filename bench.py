@@ -363,7 +363,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "seq_len": w.Lq, "heads": w.H, "head_dim": w.D,
                    "theta": w.theta, "causal": True, "rope_layout": "half", "fwd_tile": "128 queries x 64 keys",
-                   "bwd_tiles": "dQ: 128 queries x 64 keys; dK/dV: 128 keys x 32 queries"},
+                   "bwd_tiles": "dQ: 128 queries x 64 keys; dK/dV: 256 keys x 64 queries"},
         "pct_of_bf16_peak": 100 * value / configs.PEAK_BF16_TFLOPS,
         "tokens_per_s": w.B * w.Lq / (ms * 1e-3),
         "attention_fwd_tflops": w.fwd_flop() / fk["avg_ms"] / 1e9,

@@ -13,10 +13,10 @@
 //    with scores transposed (S^T = K Q^T) so each lane owns one query: P^T and dS^T are formed in
 //    registers and feed dQ^T += K^T dS^T directly; K^T operands come from the row-major K tile by
 //    transposing LDS reads.
-//  * dK/dV: a workgroup per 128-key tile (32 keys per wave) walks the visible 64-query tiles with
-//    scores in the other orientation (S = Q K^T, each lane owns one key): P and dS feed
-//    dV^T += dO^T P and dK^T += Q^T dS directly; Q^T and dO^T operands come from the row-major tiles
-//    by transposing LDS reads.
+//  * dK/dV: a workgroup per 256-key tile (32 keys per wave, their K rows held in registers) walks
+//    the visible 64-query tiles with scores in the other orientation (S = Q K^T, each lane owns one
+//    key): P and dS feed dV^T += dO^T P and dK^T += Q^T dS directly; Q^T and dO^T operands come from
+//    the row-major tiles by transposing LDS reads.
 //  With fused RoPE (lwm_blockattn_bwd_rope) the dQ and dK/dV kernels rotate their float32 dQ', dK'
 //  accumulators back by -angle just before the one rounding to bf16, so the stored gradients are
 //  w.r.t. the pre-RoPE Q and K.
@@ -273,76 +273,86 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
 }
 
 // ------------------------------------------------------------------------------ dK / dV
-// A workgroup owns 128 keys and has 8 waves, two per SIMD: wave w handles the 32 keys
-// k0 + 32 (w % 4) against the query half w / 4 of every 64-query tile, so each wave keeps one
-// 32-key dK^T and dV^T accumulator pair (128 registers) and the SIMD's two waves cover each
-// other's LDS and dependency waits.  The two partial sums of a key block are added through LDS at
-// the end.  The workgroup's K and V tiles sit in LDS for the whole pass.
-constexpr int BQ = 64;   // queries per tile
+// A workgroup owns 256 keys and has 8 waves, two per SIMD: wave w owns the 32 keys k0 + 32 w.  It
+// keeps their dK^T and dV^T accumulators (128 registers) and their K rows as MFMA operands (32
+// registers) for the whole pass; their V rows sit in LDS.  All eight waves walk the visible
+// 64-query tiles together, each tile as two 32-query sub-tiles, so every Q and dO tile brought
+// into LDS feeds the products of 256 keys: half the bytes loaded per MFMA of a 128-key workgroup,
+// and each wave's sums are complete at the end (nothing to exchange).
+constexpr int BQ = 32;   // queries per sub-tile
+constexpr int BQT = 64;  // queries per tile (two sub-tiles)
+constexpr int BKV = 256; // keys per workgroup
 constexpr int kDkdvWaves = 8;
-// One stage of the query-tile ring: the Q and dO rows of 64 queries (row-major swizzled) and the
-// queries' lse * log2(e), delta and segment ids.  The two stages and the workgroup's K / V rows are
-// LDS objects of their own, and the tile loop is unrolled by two so that every access names its
-// stage at compile time: the compiler makes a transposing LDS read wait for every load into LDS in
-// flight unless it can tell that the read's object differs from theirs, and the next tile's loads
-// are in flight for most of a step.
+constexpr int kQTileBytes = BQ * 256;  // 32 rows x 128 bf16
+// One stage of the query-tile ring: the Q and dO rows of 64 queries (row-major swizzled, sub-tile
+// u at u * kQTileBytes) and the queries' lse * log2(e), delta and segment ids.  The two stages
+// and the V rows are LDS objects of their own, and the tile loop is
+// unrolled by two so that every access names its stage at compile time: the compiler makes a
+// transposing LDS read wait for every load into LDS in flight unless it can tell that the read's
+// object differs from theirs, and the next tile's loads are in flight for most of a step.
 struct StageQO {
-  uint8_t q[kTileBytes];
-  uint8_t o[kTileBytes];
-  float lse2[BQ];
-  float dlt[BQ];
-  int32_t seg[BQ];
+  uint8_t q[2 * kQTileBytes];
+  uint8_t o[2 * kQTileBytes];
+  float lse2[64];
+  float dlt[64];
+  int32_t seg[64];
 };
-constexpr int kKVBytes = 4 * kTileBytes;  // K (128 rows) then V (128 rows)
-// after the loop: the partial-sum exchange (dK^T partials in the K/V area, dV^T partials in the two
-// stages' Q / dO areas) and each wave's epilogue staging rows (16 KB: waves 0..3 in the K/V area,
-// 4..7 in the stages) reuse the same three objects
-static_assert(kKVBytes == 4 * 4 * 4 * 64 * 16, "dK partials of 4 key blocks fill the K/V area");
-static_assert(kTileBytes == 4 * 4 * 64 * 16, "one feature block of dV partials fills a Q or dO area");
-static_assert(kTileBytes >= 32 * D * 4, "a wave's staging rows (float32) fit a Q or dO area");
+constexpr int kVBytes = BKV * 256;  // V rows of the workgroup's keys, 8 KB per wave
+// after the loop each wave stages its bf16 output rows (8 KB) in its own V rows
+static_assert(kVBytes == kDkdvWaves * 32 * D * 2, "a wave's bf16 staging rows fill its V rows");
 
 template <int S>
 using StageC = std::integral_constant<int, S>;
 
 __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams p) {
-  constexpr int BK = 128;
   __shared__ __attribute__((aligned(1024))) StageQO lds_qo0;
   __shared__ __attribute__((aligned(1024))) StageQO lds_qo1;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_kv[kKVBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_v[kVBytes];
   auto stage = [&](auto sc) __attribute__((always_inline)) -> StageQO& {
     if constexpr (decltype(sc)::value == 0) return lds_qo0;
     else return lds_qo1;
   };
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c32 = lane & 31, h32 = lane >> 5;
-  const int kb = w & 3, qh = w >> 2;  // key block of 32, query half of each 64-query tile
-  const int nkt = (p.Lk + BK - 1) / BK;
+  const int nkt = (p.Lk + BKV - 1) / BKV;
   int bh, kt;
   const bool segs = p.seg_q != nullptr;
   map_block(blockIdx.x, nkt, p.B * p.H, false, segs, bh, kt);
   const int b = bh / p.H, hh = bh - b * p.H;
-  const int k0 = kt * BK;
-  const int klast = min(k0 + BK, p.Lk) - 1;
+  const int k0 = kt * BKV;
+  const int klast = min(k0 + BKV, p.Lk) - 1;
+  const int wk0 = k0 + w * 32, wk1 = min(wk0 + 32, p.Lk) - 1;
+  const bool wave_keys = wk1 >= wk0;
+  const int krow = wk0 + c32;
 
-  // the workgroup's K and V (128 rows each) into LDS: 32 blocks of 1 KB per tensor, 4 per wave;
-  // in flight during the query-range search
+  // this wave's 32 V rows into its 8 KB of LDS (8 blocks of 1 KB; rows past the end read as zero),
+  // in flight during the query-range search; only this wave reads them
+  uint8_t* const vw = lds_v + w * 8192;
   {
-    const uint8_t* kgb = reinterpret_cast<const uint8_t*>(p.k + b * p.sk.b + hh * p.sk.h);
     const uint8_t* vgb = reinterpret_cast<const uint8_t*>(p.v + b * p.sv.b + hh * p.sv.h);
-    const int64_t klb = p.sk.l * 2, vlb = p.sv.l * 2;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kgb + k0 * klb, (int64_t)(p.Lk - 1 - k0) * klb + 256);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vgb + k0 * vlb, (int64_t)(p.Lk - 1 - k0) * vlb + 256);
+    const int64_t vlb = p.sv.l * 2;
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vgb + (int64_t)wk0 * vlb, (int64_t)(p.Lk - 1 - wk0) * vlb + 256);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int blk = w * 4 + r;
-      const int row = blk * 4 + (lane >> 4);
+    for (int r = 0; r < 8; ++r) {
+      const int row = r * 4 + (lane >> 4);
       const int c = (lane & 15) ^ swz16(row);
-      load_lds16(rk, &lds_kv[blk * 1024], (int)(row * klb) + c * 16);
-      load_lds16(rv, &lds_kv[2 * kTileBytes + blk * 1024], (int)(row * vlb) + c * 16);
+      load_lds16(rv, vw + r * 1024, (int)(row * vlb) + c * 16);
+    }
+  }
+  // this wave's K rows as the B operands of S = Q K^T: fragment sd holds features
+  // 16 sd + 8 h32 .. + 7 of key krow (zero past the end)
+  bf16x8 kreg[8];
+  {
+    const uint16_t* kg = p.k + b * p.sk.b + hh * p.sk.h + (int64_t)krow * p.sk.l;
+#pragma unroll
+    for (int sd = 0; sd < 8; ++sd) {
+      u32x4 a = {0u, 0u, 0u, 0u};
+      if (krow < p.Lk) a = *reinterpret_cast<const u32x4*>(kg + sd * 16 + h32 * 8);
+      kreg[sd] = as_bf16x8(a);
     }
   }
 
-  // queries that can see any key of this tile
+  // queries that can see any key of this workgroup
   int qbeg = 0, qend = p.Lq;
   if (p.causal) qbeg = (int)imin64(p.Lq, imax64(0, p.k_offset + k0 - p.q_offset));
   if (segs) {
@@ -358,22 +368,20 @@ __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams 
       qend = min(qend, hi);
     }
   }
-  const int t_begin = qbeg / BQ;
-  const int ntiles = (qend > qbeg) ? (qend + BQ - 1) / BQ - t_begin : 0;
+  const int t_begin = qbeg / BQT;
+  const int ntiles = (qend > qbeg) ? (qend + BQT - 1) / BQT - t_begin : 0;
 
-  const int wk0 = k0 + kb * 32, wk1 = min(wk0 + 32, p.Lk) - 1;
-  const bool wave_keys = wk1 >= wk0;
   int32_t wseg0 = 0, wseg1 = 0;
   if (segs && wave_keys) {
     wseg0 = p.seg_k[(int64_t)b * p.Lk + wk0];
     wseg1 = p.seg_k[(int64_t)b * p.Lk + wk1];
   }
-  const int krow = wk0 + c32;
-  const int64_t gk = p.k_offset + krow;
   const int32_t myseg = segs ? p.seg_k[(int64_t)b * p.Lk + min(krow, p.Lk - 1)] : 0;
-
-  const uint8_t* kw = lds_kv + kb * 8192;  // this wave's 32 keys
-  const uint8_t* vw = lds_kv + 2 * kTileBytes + kb * 8192;
+  // k_offset - q_offset for the causal mask, in 32 bits: a masked tile has some query no later than
+  // some key of the wave and some query at or after the wave's first key, which bounds it to
+  // (-2^30, 2^30 + 32) there; clamping outside that range changes no mask
+  const int kq = (int)imax64(-(int64_t(1) << 30), imin64((int64_t(1) << 30) + 64, p.k_offset - p.q_offset));
+  const int krh = krow - 4 * h32;  // this lane's key less the first query row it holds in a tile
 
   f32x16 dk[4], dv[4];
 #pragma unroll
@@ -388,29 +396,29 @@ __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams 
   const float* lse2_row = p.lse2 + ((int64_t)b * p.H + hh) * p.Lq;
   const float* dlt_row = p.delta + ((int64_t)b * p.H + hh) * p.Lq;
   const int32_t* segq_row = segs ? p.seg_q + (int64_t)b * p.Lq : nullptr;
-  // per q-tile: 16 blocks of 1 KB for Q and 16 for dO, two per wave
-  const int ld_row0 = (w * 2) * 4 + (lane >> 4), ld_row1 = ld_row0 + 4;
+  // per q-tile: 16 blocks of 1 KB for Q and 16 for dO, two of each per wave
+  const int ld_row0 = w * 8 + (lane >> 4), ld_row1 = ld_row0 + 4;
   const int ld_voff_q0 = (int)(ld_row0 * ql_bytes) + (((lane & 15) ^ swz16(ld_row0)) << 4);
   const int ld_voff_q1 = (int)(ld_row1 * ql_bytes) + (((lane & 15) ^ swz16(ld_row1)) << 4);
   const int ld_voff_o0 = (int)(ld_row0 * ol_bytes) + (((lane & 15) ^ swz16(ld_row0)) << 4);
   const int ld_voff_o1 = (int)(ld_row1 * ol_bytes) + (((lane & 15) ^ swz16(ld_row1)) << 4);
   auto issue = [&](int tile, StageQO& dst) __attribute__((always_inline)) {
-    const int q0 = tile * BQ;
+    const int q0 = tile * BQT;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(qg + q0 * ql_bytes, q_extent - q0 * ql_bytes);
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(og + q0 * ol_bytes, o_extent - q0 * ol_bytes);
-    load_lds16(rq, &dst.q[(w * 2) * 1024], ld_voff_q0);
-    load_lds16(rq, &dst.q[(w * 2 + 1) * 1024], ld_voff_q1);
-    load_lds16(ro, &dst.o[(w * 2) * 1024], ld_voff_o0);
-    load_lds16(ro, &dst.o[(w * 2 + 1) * 1024], ld_voff_o1);
+    load_lds16(rq, &dst.q[(2 * w) * 1024], ld_voff_q0);
+    load_lds16(rq, &dst.q[(2 * w + 1) * 1024], ld_voff_q1);
+    load_lds16(ro, &dst.o[(2 * w) * 1024], ld_voff_o0);
+    load_lds16(ro, &dst.o[(2 * w + 1) * 1024], ld_voff_o1);
     const int64_t rem = (int64_t)(p.Lq - q0) * 4;
     if (w == 0) load_lds4(make_rsrc(lse2_row + q0, rem), &dst.lse2[0], lane * 4);
     if (w == 1) load_lds4(make_rsrc(dlt_row + q0, rem), &dst.dlt[0], lane * 4);
     if (segs && w == 2) load_lds4(make_rsrc(segq_row + q0, rem), &dst.seg[0], lane * 4);
   };
-  // Row-major operand (Q, dO, K, V rows; row c32 within its 32-row block, chunk 2*sd + h32): the
-  // XOR swizzle leaves bit 0 of an even chunk index alone, so the offset is a per-lane base plus
-  // ((2*sd) ^ swizzle) * 16.  Transposing reads (Q^T, dO^T) for feature block db differ from block
-  // 0's offsets by an XOR of db into chunk bits 2..3.
+  // Row-major operand (Q, dO, V rows; row c32, chunk 2*sd + h32): the XOR swizzle leaves bit 0 of
+  // an even chunk index alone, so the offset is a per-lane base plus ((2*sd) ^ swizzle) * 16.
+  // Transposing reads (Q^T, dO^T) for feature block db differ from block 0's offsets by an XOR of
+  // db into chunk bits 2..3.
   const int rswz = swz16(c32 & 15);
   const int rbase = c32 * 256 + (((h32 ^ rswz) & 1) << 4);
   auto roff = [&](int sd) { return rbase + (((2 * sd) ^ (rswz & 14)) << 4); };
@@ -424,107 +432,119 @@ __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams 
   // One tile: stage S holds it, the other stage receives the next one.
   auto step = [&](auto sc, int it) __attribute__((always_inline)) {
     StageQO& cur = stage(sc);
-    const int q0 = (t_last - it) * BQ;
+    const int q0t = (t_last - it) * BQT;
     wait_vmcnt<0>();
     __syncthreads();
     if (it + 1 < ntiles) issue(t_last - it - 1, stage(StageC<1 - decltype(sc)::value>{}));
-    const uint8_t* qt = cur.q + qh * 8192;  // this wave's 32 queries
-    const uint8_t* ot = cur.o + qh * 8192;
-    const int wq0 = q0 + qh * 32;
-    bool active = wave_keys && (wq0 < p.Lq);
-    bool need_mask = false;
-    if (p.causal) {
-      active = active && (p.q_offset + wq0 + 31 >= p.k_offset + wk0);
-      need_mask = p.k_offset + wk1 > p.q_offset + wq0;
-    }
-    if (segs) {
-      const int32_t ts0 = cur.seg[qh * 32], ts1 = cur.seg[min(qh * 32 + 32, p.Lq - q0) - 1];
-      active = active && !(ts1 < wseg0 || ts0 > wseg1);
-      need_mask = need_mask || !(ts0 == ts1 && wseg0 == wseg1 && ts0 == wseg0);
-    }
-    if (!active) return;
+    // sub-tile u2: queries q0t + 32 u2 .. + 31 (none when past the end)
+    auto sub = [&](int u2) __attribute__((always_inline)) {
+      const int q0 = q0t + BQ * u2;
+      if (q0 >= p.Lq) return;
+      const uint8_t* qt = cur.q + u2 * kQTileBytes;
+      const uint8_t* ot = cur.o + u2 * kQTileBytes;
+      bool active = wave_keys;
+      bool need_mask = false;
+      if (p.causal) {
+        active = active && (p.q_offset + q0 + BQ - 1 >= p.k_offset + wk0);
+        need_mask = p.k_offset + wk1 > p.q_offset + q0;
+      }
+      if (segs) {
+        const int32_t ts0 = cur.seg[BQ * u2], ts1 = cur.seg[BQ * u2 + min(BQ, p.Lq - q0) - 1];
+        active = active && !(ts1 < wseg0 || ts0 > wseg1);
+        need_mask = need_mask || !(ts0 == ts1 && wseg0 == wseg1 && ts0 == wseg0);
+      }
+      if (!active) return;
 
-    // S = Q K^T and dP = dO V^T (32 queries x 32 keys); the four operand fragments of feature
-    // step sd + 1 are read while the two MFMAs of step sd run
-    f32x16 s, dp;
+      // S = Q K^T and dP = dO V^T (32 queries x 32 keys); the three LDS fragments of feature step
+      // sd + 1 are read while the two MFMAs of step sd run
+      f32x16 s, dp;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
-    {
-      bf16x8 f[2][4];
-      auto rd = [&](int sd, bf16x8 (&d)[4]) {
-        const int o = roff(sd);
-        d[0] = as_bf16x8(*reinterpret_cast<const u32x4*>(qt + o));
-        d[1] = as_bf16x8(*reinterpret_cast<const u32x4*>(kw + o));
-        d[2] = as_bf16x8(*reinterpret_cast<const u32x4*>(ot + o));
-        d[3] = as_bf16x8(*reinterpret_cast<const u32x4*>(vw + o));
-      };
-      rd(0, f[0]);
+      for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+      {
+        bf16x8 f[2][3];
+        auto rd = [&](int sd, bf16x8 (&d)[3]) {
+          const int o = roff(sd);
+          d[0] = as_bf16x8(*reinterpret_cast<const u32x4*>(qt + o));
+          d[1] = as_bf16x8(*reinterpret_cast<const u32x4*>(ot + o));
+          d[2] = as_bf16x8(*reinterpret_cast<const u32x4*>(vw + o));
+        };
+        rd(0, f[0]);
 #pragma unroll
-      for (int sd = 0; sd < 8; ++sd) {
-        if (sd + 1 < 8) rd(sd + 1, f[(sd + 1) & 1]);
-        __builtin_amdgcn_sched_barrier(0);
-        s = mfma_32x32x16(f[sd & 1][0], f[sd & 1][1], s);
-        dp = mfma_32x32x16(f[sd & 1][2], f[sd & 1][3], dp);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    // lane owns key krow; element i is query wq0 + acc_row(i, h32)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int r4 = qh * 32 + 8 * g + 4 * h32;
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&cur.lse2[r4]);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&cur.dlt[r4]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = 4 * g + j;
-        s[i] = __builtin_fmaf(s[i], p.scale_log2, -l4[j]);
-        dp[i] = dp[i] - d4[j];
-      }
-    }
-    if (need_mask) {
-      // element i holds query ql = qh*32 + 8*(i/4) + 4*h32 + i%4, visible iff ql >= lo (causal)
-      // and its segment matches this lane's key; masked scores get exponent -inf (a select)
-      int lo = -BQ;
-      if (p.causal) lo = (int)imax64(-BQ, imin64(BQ, gk - p.q_offset - q0));
-      lo -= qh * 32 + 4 * h32;
-      const int32_t* segt = &cur.seg[qh * 32 + 4 * h32];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        i32x4 qs = {myseg, myseg, myseg, myseg};
-        if (segs) qs = *reinterpret_cast<const i32x4*>(segt + 8 * g);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bool vis = (8 * g + j >= lo) & (qs[j] == myseg);
-          s[4 * g + j] = vis ? s[4 * g + j] : -INFINITY;
+        for (int sd = 0; sd < 8; ++sd) {
+          if (sd + 1 < 8) rd(sd + 1, f[(sd + 1) & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+          s = mfma_32x32x16(f[sd & 1][0], kreg[sd], s);
+          dp = mfma_32x32x16(f[sd & 1][1], f[sd & 1][2], dp);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
-    }
+      // lane owns key krow; element i is query q0 + acc_row(i, h32)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      s[i] = fast_exp2(s[i]);
-      dp[i] *= s[i];
-    }
-    const bf16x8 pb[2] = {pack8(s, 0), pack8(s, 1)};
-    const bf16x8 dsb[2] = {pack8(dp, 0), pack8(dp, 1)};
-    // dV^T += dO^T P, dK^T += Q^T dS (transposed operands by transposing reads, one step ahead)
-    {
-      bf16x8 g[2][2];
-      auto rdt = [&](int n, bf16x8 (&d)[2]) {
-        const int u = n >> 2, db = n & 3;
-        d[0] = read_xt(ot + u * 4096, tlo0 ^ (db << 6), thi0 ^ (db << 6));
-        d[1] = read_xt(qt + u * 4096, tlo0 ^ (db << 6), thi0 ^ (db << 6));
-      };
-      rdt(0, g[0]);
+      for (int g = 0; g < 4; ++g) {
+        const int r4 = BQ * u2 + 8 * g + 4 * h32;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&cur.lse2[r4]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&cur.dlt[r4]);
 #pragma unroll
-      for (int n = 0; n < 8; ++n) {  // n = 16-query group * 4 + feature block
-        if (n + 1 < 8) rdt(n + 1, g[(n + 1) & 1]);
-        __builtin_amdgcn_sched_barrier(0);
-        const int u = n >> 2, db = n & 3;
-        dv[db] = mfma_32x32x16(g[n & 1][0], pb[u], dv[db]);
-        dk[db] = mfma_32x32x16(g[n & 1][1], dsb[u], dk[db]);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int j = 0; j < 4; ++j) {
+          const int i = 4 * g + j;
+          s[i] = __builtin_fmaf(s[i], p.scale_log2, -l4[j]);
+          dp[i] = dp[i] - d4[j];
+        }
       }
-    }
+      if (need_mask) {
+        // element i holds query ql = 8*(i/4) + 4*h32 + i%4, visible iff q_offset + q0 + ql >=
+        // k_offset + krow (causal), i.e. 8*(i/4) + i%4 >= lo, and its segment matches this lane's
+        // key; masked scores get exponent -inf (a select).  lo stays in 32 bits: a tile needing the
+        // causal mask has kq + krow - q0 in (-2^31 + 32, 63)
+        const int lo = p.causal ? kq + (krh - q0) : -BQ;
+        // the segment ids of this lane's rows, all four groups read under one branch; the lane half's
+        // offset 4 * h32 comes from threadIdx.x itself (a value kept for the loop was spilled)
+        i32x4 qs[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) qs[g] = i32x4{myseg, myseg, myseg, myseg};
+        if (segs) {
+          const int32_t* segt = &cur.seg[BQ * u2] + ((threadIdx.x >> 3) & 4);
+#pragma unroll
+          for (int g = 0; g < 4; ++g) qs[g] = *reinterpret_cast<const i32x4*>(segt + 8 * g);
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bool vis = (8 * g + j >= lo) & (qs[g][j] == myseg);
+            s[4 * g + j] = vis ? s[4 * g + j] : -INFINITY;
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s[i] = fast_exp2(s[i]);
+        dp[i] *= s[i];
+      }
+      const bf16x8 pb[2] = {pack8(s, 0), pack8(s, 1)};
+      const bf16x8 dsb[2] = {pack8(dp, 0), pack8(dp, 1)};
+      // dV^T += dO^T P, dK^T += Q^T dS (transposed operands by transposing reads, one step ahead)
+      {
+        bf16x8 g[2][2];
+        auto rdt = [&](int n, bf16x8 (&d)[2]) {
+          const int u = n >> 2, db = n & 3;
+          d[0] = read_xt(ot + u * 4096, tlo0 ^ (db << 6), thi0 ^ (db << 6));
+          d[1] = read_xt(qt + u * 4096, tlo0 ^ (db << 6), thi0 ^ (db << 6));
+        };
+        rdt(0, g[0]);
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {  // n = 16-query group * 4 + feature block
+          if (n + 1 < 8) rdt(n + 1, g[(n + 1) & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+          const int u = n >> 2, db = n & 3;
+          dv[db] = mfma_32x32x16(g[n & 1][0], pb[u], dv[db]);
+          dk[db] = mfma_32x32x16(g[n & 1][1], dsb[u], dk[db]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
+    sub(0);
+    sub(1);
   };
   if (ntiles > 0) issue(t_last, lds_qo0);
   int it = 0;
@@ -533,59 +553,41 @@ __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams 
     step(StageC<1>{}, it + 1);
   }
   if (it < ntiles) step(StageC<0>{}, it);
+  wait_vmcnt<0>();  // this wave's V rows, when no tile was visited
   __syncthreads();
-  // add the second query half's partial sums (waves 4..7) to the first's (waves 0..3) via LDS:
-  // dK^T partials in the K/V area [key block][db][16 groups of 4][64 lanes], dV^T partials of
-  // feature block db in the Q (db even) or dO (db odd) area of stage db / 2, [key block][group][lane]
-  auto xdk = [&](int db, int g) __attribute__((always_inline)) {
-    return reinterpret_cast<f32x4*>(lds_kv) + ((kb * 4 + db) * 4 + g) * 64 + lane;
-  };
-  auto xdv = [&](int db, int g) __attribute__((always_inline)) {
-    uint8_t* area = db == 0 ? lds_qo0.q : db == 1 ? lds_qo0.o : db == 2 ? lds_qo1.q : lds_qo1.o;
-    return reinterpret_cast<f32x4*>(area) + (kb * 4 + g) * 64 + lane;
-  };
-  if (qh == 1) {
+
+  const int rows_valid = max(0, min(32, p.Lk - wk0));
+  if (p.dk_acc) {
+    // backward ring step: dK, dV += this query block's share, in float32.  Lane c32 owns key row
+    // wk0 + c32; accumulator element 4g + j of block db is feature db*32 + 8g + 4*h32 + j, so each
+    // (db, g) is one 16-byte read-add-write of the row (rows belong to this wave alone).
+    auto add_row = [&](const f32x16 (&acc)[4], float mul, float* row) __attribute__((always_inline)) {
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        *xdk(db, g) = f32x4{dk[db][4 * g], dk[db][4 * g + 1], dk[db][4 * g + 2], dk[db][4 * g + 3]};
-        *xdv(db, g) = f32x4{dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]};
-      }
-  }
-  __syncthreads();
-  if (qh == 0) {
+        for (int g = 0; g < 4; ++g) {
+          f32x4* a = reinterpret_cast<f32x4*>(row + db * 32 + 8 * g + 4 * h32);
+          f32x4 x = *a;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 a = *xdk(db, g);
-        const f32x4 c = *xdv(db, g);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          dk[db][4 * g + j] += a[j];
-          dv[db][4 * g + j] += c[j];
+          for (int j = 0; j < 4; ++j) x[j] = __builtin_fmaf(acc[db][4 * g + j], mul, x[j]);
+          *a = x;
         }
-      }
-  }
-  __syncthreads();
-  // waves 0..3 store (the row helpers have block-wide barriers: every wave takes part)
-  const int rows_valid = qh == 0 ? max(0, min(32, p.Lk - wk0)) : 0;
-  // staging rows (16 KB per wave): waves 0..3 in the K/V area, 4..7 in the stages' Q / dO areas
-  uint8_t* const stage_w = w < 4 ? lds_kv + w * (32 * D * 4)
-                                 : (w == 4 ? lds_qo0.q : w == 5 ? lds_qo0.o : w == 6 ? lds_qo1.q : lds_qo1.o);
-  if (p.dk_acc) {  // backward ring step: dK, dV += this query block's share, in float32
-    add_rows_f32(stage_w, dk, p.scale, p.dk_acc + b * p.sdka.b + hh * p.sdka.h + wk0 * p.sdka.l, p.sdka.l, rows_valid);
-    add_rows_f32(stage_w, dv, 1.f, p.dv_acc + b * p.sdva.b + hh * p.sdva.h + wk0 * p.sdva.l, p.sdva.l, rows_valid);
+    };
+    if (c32 < rows_valid) {
+      add_row(dk, p.scale, p.dk_acc + b * p.sdka.b + hh * p.sdka.h + (int64_t)krow * p.sdka.l);
+      add_row(dv, 1.f, p.dv_acc + b * p.sdva.b + hh * p.sdva.h + (int64_t)krow * p.sdva.l);
+    }
   } else {
-    if (p.rope.on && qh == 0) {  // dK' -> dK (inverse RoPE of the key rows) before rounding to bf16
+    if (p.rope.on) {  // dK' -> dK (inverse RoPE of the key rows) before rounding to bf16
       const bool restart = segs && p.rope.restart;
       const int64_t pos = rope_row_position(restart ? p.seg_k + (int64_t)b * p.Lk : nullptr, p.Lk, wk0, restart,
                                             p.rope.k_pos_offset);
       rope_unrotate_acc(dk, pos, p.rope, h32);
     }
-    store_rows_bf16(stage_w, dk, p.scale, p.dk + b * p.sdk.b + hh * p.sdk.h + wk0 * p.sdk.l, p.sdk.l, rows_valid);
-    store_rows_bf16(stage_w, dv, 1.f, p.dv + b * p.sdv.b + hh * p.sdv.h + wk0 * p.sdv.l, p.sdv.l, rows_valid);
+    // staging rows: the wave's own V rows (the row helpers have block-wide barriers: every wave
+    // takes part)
+    store_rows_bf16(vw, dk, p.scale, p.dk + b * p.sdk.b + hh * p.sdk.h + wk0 * p.sdk.l, p.sdk.l, rows_valid);
+    store_rows_bf16(vw, dv, 1.f, p.dv + b * p.sdv.b + hh * p.sdv.h + wk0 * p.sdv.l, p.sdv.l, rows_valid);
   }
 }
 
@@ -600,7 +602,7 @@ hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t stream) {
     LWM_LAUNCH("bwd_dq", bwd_dq_kernel, dim3(nqt * p.B * p.H), dim3(kThreads), stream, p);
   }
   if (p.Lk > 0) {
-    const int nkt = (p.Lk + 127) / 128;
+    const int nkt = (p.Lk + BKV - 1) / BKV;
     LWM_LAUNCH("bwd_dkdv", bwd_dkdv_kernel, dim3(nkt * p.B * p.H), dim3(kDkdvWaves * kWave), stream, p);
   }
   return hipGetLastError();
