@@ -59,6 +59,15 @@ def test_offsets(offsets, lens):
     bwd_case(1, lens[0], lens[1], 2, 2200 + sum(offsets), q_offset=offsets[0], k_offset=offsets[1])
 
 
+@pytest.mark.parametrize("offsets,lens", [((1 << 33, 1 << 33), (300, 300)), (((1 << 33) + 300, 1 << 33), (200, 520)),
+                                          (((1 << 31) + 77, 0), (150, 290)), ((5, (1 << 31) + 3), (130, 260))])
+def test_large_offsets(offsets, lens):
+    """Global positions far beyond 32 bits: the diagonal at 2^33, queries 300 past the keys there,
+    queries 2^31 past the keys (every pair visible) and keys 2^31 past the queries (none)."""
+    need_gpu()
+    bwd_case(1, lens[0], lens[1], 2, 2250 + lens[0], q_offset=offsets[0], k_offset=offsets[1])
+
+
 def test_noncausal_and_heads():
     need_gpu()
     bwd_case(1, 190, 77, 2, 2301, causal=False)

@@ -75,6 +75,17 @@ def test_offsets(dtype, offsets):
     run_case(dtype, 1, 150, 270, 2, 400 + qo + ko, q_offset=qo, k_offset=ko)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("offsets", [(1 << 33, 1 << 33), ((1 << 33) + 300, 1 << 33), ((1 << 31) + 77, 0),
+                                     (5, (1 << 31) + 3)])
+def test_large_offsets(dtype, offsets):
+    """Global positions far beyond 32 bits (diagonal at 2^33, queries 2^31 past the keys, keys 2^31
+    past the queries)."""
+    need_gpu()
+    qo, ko = offsets
+    run_case(dtype, 1, 170, 330, 2, 450 + (qo + ko) % 97, q_offset=qo, k_offset=ko)
+
+
 def test_custom_scale_and_batch_heads():
     need_gpu()
     run_case("bf16", 3, 200, 200, 5, 501, scale=0.05)
