@@ -41,9 +41,9 @@ def hipcc() -> str:
 SOURCE_FLAGS = {"attn_bwd.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
 
 
-def _compile(src: str, extra=()) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, extra=(), bdir: str = BUILD) -> str:
+    os.makedirs(bdir, exist_ok=True)
+    obj = os.path.join(bdir, os.path.splitext(src)[0] + ".o")
     cmd = [hipcc(), *HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), *extra, "-I", os.path.join(ROOT, "include"), "-c",
            os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
@@ -54,23 +54,35 @@ def _compile(src: str, extra=()) -> str:
     return obj
 
 
-def build(verbose: bool = True, save_temps: bool = False) -> str:
+# Host-side AddressSanitizer for the checking build (device code is built as usual).
+HOST_ASAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build(verbose: bool = True, save_temps: bool = False, host_asan: bool = False) -> str:
+    """Compile and link the library.  With host_asan the host code (argument checks, timing) is
+    instrumented by AddressSanitizer and the library goes to _build/asan/liblwm_attn.so instead
+    of the package; load it with LWM_ATTN_LIB and the sanitizer runtime preloaded."""
     extra = ["-save-temps=obj"] if save_temps else []
+    bdir, out = BUILD, LIB
+    if host_asan:
+        extra = extra + HOST_ASAN
+        bdir = os.path.join(BUILD, "asan")
+        out = os.path.join(bdir, "liblwm_attn.so")
     with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+        objs = list(ex.map(lambda s: _compile(s, extra, bdir), SOURCES))
+    tmp = out + ".tmp"
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *(HOST_ASAN if host_asan else []), *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":
-    build(save_temps="--save-temps" in sys.argv)
+    build(save_temps="--save-temps" in sys.argv, host_asan="--host-asan" in sys.argv)
 
 
 # Kernel sources per family of kernels: a counter record taken on one family stays valid while
