@@ -16,14 +16,14 @@ pytestmark = pytest.mark.gpu
 N_CASES = 48
 
 
-def draw_cases(seed=20261203, n=N_CASES):
+def draw_cases(seed=20261203, n=N_CASES, hmax=3, lmax=700, seed0=5000):
     rng = np.random.default_rng(seed)
     cases = []
     for i in range(n):
         B = int(rng.integers(1, 3))
-        H = int(rng.integers(1, 4))
-        Lq = int(rng.integers(1, 701))
-        Lk = Lq if rng.random() < 0.5 else int(rng.integers(1, 701))
+        H = int(rng.integers(1, hmax + 1))
+        Lq = int(rng.integers(1, lmax + 1))
+        Lk = Lq if rng.random() < 0.5 else int(rng.integers(1, lmax + 1))
         causal = bool(rng.random() < 0.75)
         q_offset = int(rng.integers(0, 601)) if rng.random() < 0.5 else 0
         k_offset = int(rng.integers(0, 601)) if rng.random() < 0.5 else 0
@@ -34,11 +34,13 @@ def draw_cases(seed=20261203, n=N_CASES):
             sk = sq.copy() if Lk == Lq else np.sort(rng.integers(0, nseg, size=(B, Lk)), axis=1).astype(np.int32)
             seg = (sq, sk)
         cases.append(dict(B=B, H=H, Lq=Lq, Lk=Lk, causal=causal, q_offset=q_offset, k_offset=k_offset, seg=seg,
-                          seed=5000 + i))
+                          seed=seed0 + i))
     return cases
 
 
-CASES = draw_cases()
+# a second draw with up to 4 heads (so B*H reaches 8, the XCD-grouped block orders) and up to
+# 1100 rows (several 256-key workgroups of the dK/dV kernel)
+CASES = draw_cases() + draw_cases(seed=20261206, n=24, hmax=4, lmax=1100, seed0=5500)
 
 
 def case_id(c):
