@@ -215,11 +215,13 @@ def test_grid_bound_covers_key_tiles():
     assert st == -2 and "grid too large" in L.lwm_last_error().decode(), L.lwm_last_error()
     st = L.lwm_blockattn_fwd(r(q), r(k), r(k), None, None, 0, 0, 1, 0.0, r(q), None, None)
     assert st == -2 and "grid too large" in L.lwm_last_error().decode()
-    # the same sizes with a small batch fit
+    # the same sizes with a small batch pass the grid bound: the call gets as far as a later check
+    # (a negative scale) and is refused there.  No call in this file may pass every check: its
+    # descriptors point at address 16, and a launch on a machine with a GPU would fault it.
     q1 = t4(B=1, L=1, H=2)
     k1 = t4(B=1, L=1 << 20, H=2)
-    assert L.lwm_blockattn_fwd(r(q1), r(k1), r(k1), None, None, 0, 0, 1, 0.0, r(q1), None, None) != -2 or \
-        "grid" not in L.lwm_last_error().decode()
+    st = L.lwm_blockattn_fwd(r(q1), r(k1), r(k1), None, None, 0, 0, 1, -1.0, r(q1), None, None)
+    assert st == -1 and "scale" in L.lwm_last_error().decode(), L.lwm_last_error()
 
 
 def test_binding_rejects_host_and_misshapen_tensors():
@@ -264,3 +266,27 @@ def test_noalloc_backward_size_limit():
     st = L.lwm_blockattn_bwd_noalloc(r(q), r(q), r(q), r(q), 16, r(q), None, None, 0, 0, 1, 0.0, r(q), r(q), r(q),
                                      None)
     assert st == -2 and "static workspace" in L.lwm_last_error().decode()
+
+
+@pytest.mark.parametrize("src,sink,blocks,iters,needle", [
+    (None, 16, 4, 64, "NULL"),
+    (16, None, 4, 64, "NULL"),
+    (8, 16, 4, 64, "aligned"),
+    (16, 2, 4, 64, "aligned"),
+    (16, 16, 0, 64, "blocks"),
+    (16, 16, 65536, 64, "blocks"),
+    (16, 16, 4, 0, "iters"),
+    (16, 16, 4, 12, "iters"),
+    (16, 16, 4, (1 << 30) + 8, "iters"),
+])
+def test_mfma_probe_validation(src, sink, blocks, iters, needle):
+    """The matrix-core rate probe checks its arguments on the host and launches nothing otherwise."""
+    L = _lib()
+    st = L.lwm_probe_mfma_bf16(src, sink, blocks, iters, None)
+    assert st == -1 and needle in L.lwm_last_error().decode()
+
+
+def test_mfma_probe_binding_rejects_host_and_misshapen_tensors():
+    import torch
+    with pytest.raises(ValueError, match="GPU tensor"):
+        lwm.lwm_probe_mfma_bf16(torch.zeros(256 * 128, dtype=torch.bfloat16), 8)
