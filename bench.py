@@ -8,9 +8,10 @@ seeded N(0,1) and resident in HBM before the timed region.  ``value`` is algorit
 causal-attention TFLOP/s of forward + backward (visible pairs only, 4*D + 10*D flop per pair).
 
 Also reported: per-kernel durations from HIP events recorded around every launch on its
-stream during the timed steps, the roofline of the dominant kernel, the CPU oracle timed on a
-bounded sample of the same workload, and (unless --no-extras) the forward-only, packed, ring
-and feed-forward workloads as extra lines inside the same JSON object.
+stream during the timed steps, the roofline of the dominant kernel, what the matrix cores
+sustain on this machine with nothing else in the loop (random N(0,1) and constant operands), the CPU
+oracle timed on a bounded sample of the same workload, and (unless --no-extras) the
+forward-only, packed, ring and feed-forward workloads as extra lines inside the same JSON object.
 """
 from __future__ import annotations
 
@@ -84,6 +85,27 @@ def time_settled(step, steps, warmup, lwm, torch, warm_ms=300.0, timed_ms=600.0)
     k = max(steps, math.ceil(timed_ms / one))
     ms, prof = time_steps(step, k, w, lwm, torch)
     return ms, prof, k, w
+
+
+def mfma_ceiling(torch, lwm, configs, blocks=512, iters=131072):
+    """What the bf16 matrix cores sustain on this machine with nothing else in the loop
+    (lwm_probe_mfma_bf16: 4 independent 32x32x16 MFMA chains per wave, two waves per SIMD,
+    operands in registers), for N(0,1) operands like the attention's Q, K, V and dO, and for a
+    constant operand.  The chip holds a lower clock under its power limit when more operand bits
+    toggle, so this, not the rated peak, is the most any kernel on these inputs can reach."""
+    out = {"unit": "TFLOP/s", "peak": configs.PEAK_BF16_TFLOPS, "blocks": blocks, "iters": iters}
+    n = blocks * 256 * 128
+    g = torch.Generator(device="cuda").manual_seed(20261203)
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    flop = blocks * 4 * iters * 4 * 32768
+    for name, src in (("random_normal", torch.randn(n, generator=g, device="cuda").to(torch.bfloat16)),
+                      ("constant", torch.full((n,), 0.01, device="cuda", dtype=torch.bfloat16))):
+        _, prof, k, wu = time_settled(lambda: lwm.lwm_probe_mfma_bf16(src, iters, sink), 3, 1, lwm, torch)
+        total_ms, launches = prof["mfma_probe"]
+        out[name] = flop / (total_ms / launches * 1e-3) / 1e12
+        out[name + "_frac"] = out[name] / configs.PEAK_BF16_TFLOPS
+        out[name + "_launches"] = launches
+    return out
 
 
 def kernels_table(prof, steps):
@@ -318,6 +340,7 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="skip the forward / packed / ring lines")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=1, help="heads of the oracle sample")
+    ap.add_argument("--no-mfma-ceiling", action="store_true", help="skip the matrix-core rate probe")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -385,6 +408,9 @@ def main():
         "tokens_per_s": w.B * w.Lq / (fms * 1e-3),
         "note": "same workload and flop count as the headline step; dQ and dK rounded to bf16 once",
         "kernels": fks}
+    if not args.no_mfma_ceiling:
+        log("[bench] matrix-core rate probe")
+        result["mfma_ceiling"] = mfma_ceiling(torch, lwm, configs)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(w, h, w.theta, heads=args.cpu_heads)

@@ -305,6 +305,28 @@ int lwm_profile_reset(void);
 int lwm_profile_count(void);
 int lwm_profile_get(int32_t index, const char** name, double* total_ms, int64_t* launches);
 
+/*
+ * Matrix-core rate probe (instrumentation, not part of the method).  Launches `blocks`
+ * workgroups of four waves (64 lanes each) on `stream`.  Every wave runs `iters` rounds of four
+ * independent v_mfma_f32_32x32x16_bf16 (a 32x16 by 16x32 bf16 product added into a 32x32
+ * float32 accumulator, 32768 flop), with A and B operands rotating over eight fragments each
+ * that every lane reads once, before the loop, from `src`; the loop itself does nothing else.
+ * A launch therefore performs blocks * 4 * iters * 4 * 32768 flop, and its duration on the
+ * stream gives the rate the matrix cores sustain for those operand values (the clock the chip
+ * holds depends on them).  Each workgroup reserves 96 KB of LDS, so a CU runs one at a time and
+ * each of its waves has a SIMD's matrix core to itself; on a 256-CU part 256 blocks fill the
+ * chip once, 512 twice.
+ *   src:  device bf16, blocks * 256 * 128 values (lane t of the grid reads values
+ *         128 t .. 128 t + 127: eight A fragments of 8, then eight B fragments of 8),
+ *         16-byte aligned, owned by the caller.
+ *   sink: device float32, blocks * 256 values, written with each lane's sum of its final
+ *         accumulators (so the products cannot be optimised away).
+ *   iters: a positive multiple of 8, at most 2^30.
+ * Returns LWM_OK, LWM_ERR_INVALID_ARG for a NULL or misaligned pointer, blocks outside
+ * [1, 65535] or a bad iters, LWM_ERR_HIP if the launch fails.
+ */
+int lwm_probe_mfma_bf16(const void* src, void* sink, int32_t blocks, int32_t iters, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -18,7 +18,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblwm_attn.so")
 ARCH = "gfx950"
 
-SOURCES = ["abi.cpp", "profile.cpp", "rope.hip", "attn_fwd.hip", "attn_bwd.hip", "ffn.hip"]
+SOURCES = ["abi.cpp", "profile.cpp", "rope.hip", "attn_fwd.hip", "attn_bwd.hip", "ffn.hip", "probe.hip"]
 
 # Packed-FP32 VALU forms are disabled for device code; the host pass ignores the feature.
 HIPCC_FLAGS = [

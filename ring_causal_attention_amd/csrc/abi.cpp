@@ -12,6 +12,11 @@
 #include "../../include/lwm_attn.h"
 #include "kernels.hpp"
 
+namespace lwm {
+// matrix-core rate probe (probe.hip): instrumentation, kept apart from the kernels' header
+hipError_t launch_mfma_probe(const void* src, float* sink, int blocks, int iters, hipStream_t stream);
+}  // namespace lwm
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -485,6 +490,16 @@ int lwm_blockwise_ffn(const void* x, int64_t rows, int64_t d_model, int64_t ldx,
   p.rows = rows; p.chunk = chunk < rows ? chunk : rows;
   p.d_model = (int)d_model; p.d_ff = (int)d_ff;
   return hip_status(lwm::launch_ffn(p, static_cast<hipStream_t>(stream)), "feed-forward launch");
+}
+
+int lwm_probe_mfma_bf16(const void* src, void* sink, int32_t blocks, int32_t iters, void* stream) {
+  if (!src || !sink) return fail(LWM_ERR_INVALID_ARG, "src and sink must not be NULL");
+  if (reinterpret_cast<uintptr_t>(src) % 16 || reinterpret_cast<uintptr_t>(sink) % 4)
+    return fail(LWM_ERR_INVALID_ARG, "src must be 16-byte and sink 4-byte aligned");
+  if (blocks < 1 || blocks > 65535) return fail(LWM_ERR_INVALID_ARG, "blocks must be in [1, 65535]");
+  if (iters < 8 || iters % 8 || iters > (1 << 30)) return fail(LWM_ERR_INVALID_ARG, "iters must be a positive multiple of 8, at most 2^30");
+  return hip_status(lwm::launch_mfma_probe(src, static_cast<float*>(sink), blocks, iters, static_cast<hipStream_t>(stream)),
+                    "MFMA probe launch");
 }
 
 }  // extern "C"

@@ -42,7 +42,8 @@ _lib = None
 EXPORTS = ["lwm_abi_version", "lwm_last_error", "lwm_rope_apply", "lwm_blockattn_fwd",
            "lwm_blockattn_bwd_workspace_size", "lwm_blockattn_bwd", "lwm_blockattn_bwd_noalloc", "lwm_blockattn_fwd_rope",
            "lwm_blockattn_bwd_rope", "lwm_ring_step", "lwm_ring_step_bwd",
-           "lwm_blockwise_ffn_workspace_size", "lwm_blockwise_ffn", "lwm_profile_enable", "lwm_profile_reset", "lwm_profile_count", "lwm_profile_get"]
+           "lwm_blockwise_ffn_workspace_size", "lwm_blockwise_ffn", "lwm_profile_enable", "lwm_profile_reset", "lwm_profile_count", "lwm_profile_get",
+           "lwm_probe_mfma_bf16"]
 
 
 def lib() -> ctypes.CDLL:
@@ -91,6 +92,8 @@ def lib() -> ctypes.CDLL:
     L.lwm_profile_count.argtypes = []
     L.lwm_profile_get.restype = ctypes.c_int
     L.lwm_profile_get.argtypes = [I32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(F64), ctypes.POINTER(I64)]
+    L.lwm_probe_mfma_bf16.restype = ctypes.c_int
+    L.lwm_probe_mfma_bf16.argtypes = [VP, VP, I32, I32, VP]
     _lib = L
     return L
 
@@ -382,3 +385,21 @@ def lwm_profile_read() -> dict:
         _check(L.lwm_profile_get(i, ctypes.byref(name), ctypes.byref(ms), ctypes.byref(n)))
         out[name.value.decode()] = (ms.value, n.value)
     return out
+
+
+def lwm_probe_mfma_bf16(src: torch.Tensor, iters: int, sink: torch.Tensor | None = None) -> torch.Tensor:
+    """Matrix-core rate probe: ``src`` is a bf16 GPU tensor of blocks * 256 * 128 values; one
+    launch of blocks = src.numel() // 32768 workgroups, each wave ``iters`` rounds of four
+    32x32x16 bf16 MFMAs on register-resident operands read from ``src``.  Returns ``sink``
+    (float32, one value per lane)."""
+    _on_device(src, "src", None)
+    if src.dtype != torch.bfloat16 or not src.is_contiguous() or src.numel() % (256 * 128) or src.numel() == 0:
+        raise ValueError("src: expected a contiguous bf16 GPU tensor of blocks * 256 * 128 values")
+    blocks = src.numel() // (256 * 128)
+    if sink is None:
+        sink = torch.empty(blocks * 256, dtype=torch.float32, device=src.device)
+    _on_device(sink, "sink", src.device)
+    if sink.dtype != torch.float32 or not sink.is_contiguous() or sink.numel() != blocks * 256:
+        raise ValueError(f"sink: expected a contiguous float32 GPU tensor of {blocks * 256} values")
+    _check(lib().lwm_probe_mfma_bf16(_ptr(src), _ptr(sink), blocks, int(iters), _stream(src)))
+    return sink
