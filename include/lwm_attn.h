@@ -321,9 +321,10 @@ int lwm_profile_get(int32_t index, const char** name, double* total_ms, int64_t*
  *         16-byte aligned, owned by the caller.
  *   sink: device float32, blocks * 256 values, written with each lane's sum of its final
  *         accumulators (so the products cannot be optimised away).
- *   iters: a positive multiple of 8, at most 2^30.
+ *   iters: a positive multiple of 8, at most 2^24 (with blocks <= 4096, a launch stays within
+ *          about 20 s on a 256-CU part).
  * Returns LWM_OK, LWM_ERR_INVALID_ARG for a NULL or misaligned pointer, blocks outside
- * [1, 65535] or a bad iters, LWM_ERR_HIP if the launch fails.
+ * [1, 4096] or a bad iters, LWM_ERR_HIP if the launch fails.
  */
 int lwm_probe_mfma_bf16(const void* src, void* sink, int32_t blocks, int32_t iters, void* stream);
 

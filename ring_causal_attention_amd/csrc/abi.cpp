@@ -496,8 +496,9 @@ int lwm_probe_mfma_bf16(const void* src, void* sink, int32_t blocks, int32_t ite
   if (!src || !sink) return fail(LWM_ERR_INVALID_ARG, "src and sink must not be NULL");
   if (reinterpret_cast<uintptr_t>(src) % 16 || reinterpret_cast<uintptr_t>(sink) % 4)
     return fail(LWM_ERR_INVALID_ARG, "src must be 16-byte and sink 4-byte aligned");
-  if (blocks < 1 || blocks > 65535) return fail(LWM_ERR_INVALID_ARG, "blocks must be in [1, 65535]");
-  if (iters < 8 || iters % 8 || iters > (1 << 30)) return fail(LWM_ERR_INVALID_ARG, "iters must be a positive multiple of 8, at most 2^30");
+  // bounded so that one launch stays within seconds (4096 blocks of 2^24 rounds: about 20 s on a 256-CU part)
+  if (blocks < 1 || blocks > 4096) return fail(LWM_ERR_INVALID_ARG, "blocks must be in [1, 4096]");
+  if (iters < 8 || iters % 8 || iters > (1 << 24)) return fail(LWM_ERR_INVALID_ARG, "iters must be a positive multiple of 8, at most 2^24");
   return hip_status(lwm::launch_mfma_probe(src, static_cast<float*>(sink), blocks, iters, static_cast<hipStream_t>(stream)),
                     "MFMA probe launch");
 }

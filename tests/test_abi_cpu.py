@@ -274,10 +274,10 @@ def test_noalloc_backward_size_limit():
     (8, 16, 4, 64, "aligned"),
     (16, 2, 4, 64, "aligned"),
     (16, 16, 0, 64, "blocks"),
-    (16, 16, 65536, 64, "blocks"),
+    (16, 16, 4097, 64, "blocks"),
     (16, 16, 4, 0, "iters"),
     (16, 16, 4, 12, "iters"),
-    (16, 16, 4, (1 << 30) + 8, "iters"),
+    (16, 16, 4, (1 << 24) + 8, "iters"),
 ])
 def test_mfma_probe_validation(src, sink, blocks, iters, needle):
     """The matrix-core rate probe checks its arguments on the host and launches nothing otherwise."""
