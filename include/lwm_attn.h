@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define LWM_ABI_VERSION 5
+#define LWM_ABI_VERSION 6
 
 typedef enum {
   LWM_OK = 0,
@@ -202,16 +202,21 @@ int lwm_ring_step(const lwm_tensor4* q, const lwm_tensor4* k_shard, const lwm_te
  * scale as in lwm_blockattn_fwd.  dq_acc (like q) and dk_acc, dv_acc (like k_shard) are
  * float32 lwm_tensor4 views that are read and added to (the caller zeroes them before the first
  * step); results are w.r.t. the rotated operands, as for lwm_blockattn_bwd.  workspace: at
- * least lwm_blockattn_bwd_workspace_size(B, H, Lq, Lk, D) bytes, 256-byte aligned (D and the
- * rescaled lse are recomputed into it on every call).  Errors as for lwm_blockattn_bwd; a
- * shard wholly in the causal future adds zero.
+ * least lwm_blockattn_bwd_workspace_size(B, H, Lq, Lk, D) bytes, 256-byte aligned; the call
+ * writes D and the rescaled lse of the query block into it.  Both depend on the query block only,
+ * so the steps of one ring after the first may pass flags = LWM_RING_BWD_REUSE_WORKSPACE to use
+ * what the first step wrote instead of recomputing it (same workspace, and the same q, o, lse,
+ * dout and shape as that step; the library cannot check this).  flags: 0 or
+ * LWM_RING_BWD_REUSE_WORKSPACE.  Errors as for lwm_blockattn_bwd, LWM_ERR_INVALID_ARG for other
+ * flags; a shard wholly in the causal future adds zero.
  */
+#define LWM_RING_BWD_REUSE_WORKSPACE 1
 int lwm_ring_step_bwd(const lwm_tensor4* q, const lwm_tensor4* k_shard, const lwm_tensor4* v_shard,
                       const lwm_tensor4* o, const float* lse, const lwm_tensor4* dout,
                       const int32_t* seg_q, const int32_t* seg_k, int64_t q_offset,
                       int64_t k_offset, int32_t causal, float scale, const lwm_tensor4* dq_acc,
                       const lwm_tensor4* dk_acc, const lwm_tensor4* dv_acc, void* workspace,
-                      size_t workspace_bytes, void* stream);
+                      size_t workspace_bytes, int32_t flags, void* stream);
 
 /*
  * RoPE inside the attention kernels (the two entry points below).  RoPE with theta scaled to

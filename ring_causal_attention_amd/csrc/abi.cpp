@@ -393,9 +393,11 @@ int lwm_ring_step_bwd(const lwm_tensor4* q, const lwm_tensor4* k_shard, const lw
                       const lwm_tensor4* o, const float* lse, const lwm_tensor4* dout, const int32_t* seg_q,
                       const int32_t* seg_k, int64_t q_offset, int64_t k_offset, int32_t causal, float scale,
                       const lwm_tensor4* dq_acc, const lwm_tensor4* dk_acc, const lwm_tensor4* dv_acc,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+                      void* workspace, size_t workspace_bytes, int32_t flags, void* stream) {
   lwm::BwdParams p;
   int s;
+  if (flags != 0 && flags != LWM_RING_BWD_REUSE_WORKSPACE)
+    return fail(LWM_ERR_INVALID_ARG, "flags must be 0 or LWM_RING_BWD_REUSE_WORKSPACE");
   if ((s = prepare_bwd(q, k_shard, v_shard, o, lse, dout, seg_q, seg_k, q_offset, k_offset, causal, scale, workspace,
                        workspace_bytes, &p)))
     return s;
@@ -406,6 +408,7 @@ int lwm_ring_step_bwd(const lwm_tensor4* q, const lwm_tensor4* k_shard, const lw
   p.dk_acc = static_cast<float*>(dk_acc->ptr);
   p.dv_acc = static_cast<float*>(dv_acc->ptr);
   p.sdqa = strides(dq_acc); p.sdka = strides(dk_acc); p.sdva = strides(dv_acc);
+  p.delta_ready = flags == LWM_RING_BWD_REUSE_WORKSPACE;
   return hip_status(lwm::launch_attn_bwd(p, static_cast<hipStream_t>(stream)), "backward ring step launch");
 }
 

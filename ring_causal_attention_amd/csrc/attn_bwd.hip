@@ -597,7 +597,8 @@ hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t stream) {
   if (p.B == 0 || p.H == 0) return hipSuccess;
   if (p.Lq > 0) {
     const int64_t rows = (int64_t)p.B * p.Lq * p.H;
-    LWM_LAUNCH("bwd_delta", bwd_delta_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), stream, p);
+    if (!p.delta_ready)
+      LWM_LAUNCH("bwd_delta", bwd_delta_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), stream, p);
     const int nqt = (p.Lq + 127) / 128;
     LWM_LAUNCH("bwd_dq", bwd_dq_kernel, dim3(nqt * p.B * p.H), dim3(kThreads), stream, p);
   }

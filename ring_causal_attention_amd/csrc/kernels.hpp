@@ -93,6 +93,8 @@ struct BwdParams {
   float* dk_acc;
   float* dv_acc;
   Strides sdqa, sdka, sdva;
+  // set when delta and lse2 already hold this query block's values (a later step of one ring)
+  int delta_ready;
   // rope.on: dq and dk are rotated back (inverse RoPE) before they are stored, so they are
   // gradients w.r.t. the pre-RoPE Q and K (stored outputs only, not the ring accumulators)
   RopeFuse rope;

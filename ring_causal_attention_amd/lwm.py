@@ -79,7 +79,8 @@ def lib() -> ctypes.CDLL:
     L.lwm_ring_step.restype = ctypes.c_int
     L.lwm_ring_step.argtypes = [P, P, P, VP, VP, I64, I64, I32, F32, P, VP, P, VP]
     L.lwm_ring_step_bwd.restype = ctypes.c_int
-    L.lwm_ring_step_bwd.argtypes = [P, P, P, P, VP, P, VP, VP, I64, I64, I32, F32, P, P, P, VP, ctypes.c_size_t, VP]
+    L.lwm_ring_step_bwd.argtypes = [P, P, P, P, VP, P, VP, VP, I64, I64, I32, F32, P, P, P, VP, ctypes.c_size_t, I32,
+                                    VP]
     L.lwm_blockwise_ffn_workspace_size.restype = ctypes.c_size_t
     L.lwm_blockwise_ffn_workspace_size.argtypes = [I64, I64, I64]
     L.lwm_blockwise_ffn.restype = ctypes.c_int
@@ -314,13 +315,20 @@ def lwm_ring_step(q, k_shard, v_shard, o_acc, lse_acc, seg_q=None, seg_k=None, q
     return o_acc, lse_acc
 
 
+RING_BWD_REUSE_WORKSPACE = 1
+
+
 def lwm_ring_step_bwd(q, k_shard, v_shard, o, lse, dout, dq_acc, dk_acc, dv_acc, seg_q=None, seg_k=None,
-                      q_offset=0, k_offset=0, causal=True, scale=0.0, workspace=None):
+                      q_offset=0, k_offset=0, causal=True, scale=0.0, workspace=None, reuse_workspace=False):
     """Add one KV shard's share of the gradients into dq_acc (float32, like q) and dk_acc,
-    dv_acc (float32, like k_shard), in place; o and lse are the forward's results over all shards."""
+    dv_acc (float32, like k_shard), in place; o and lse are the forward's results over all shards.
+    ``reuse_workspace``: the workspace already holds this query block's delta and rescaled lse
+    from an earlier step of the same ring (same q, o, lse, dout), so that pass is skipped."""
     B, Lq, H, D = q.shape
     need = lwm_blockattn_bwd_workspace_size(B, H, Lq, k_shard.shape[1], D)
     if workspace is None:
+        if reuse_workspace:
+            raise ValueError("reuse_workspace needs the workspace an earlier step of the ring wrote")
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     d, Lk = q.device, k_shard.shape[1]
     _check(lib().lwm_ring_step_bwd(_ref(tensor4(q, "q", d)), _ref(tensor4(k_shard, "k_shard", d)),
@@ -330,7 +338,8 @@ def lwm_ring_step_bwd(q, k_shard, v_shard, o, lse, dout, dq_acc, dk_acc, dv_acc,
                                    int(q_offset), int(k_offset), int(bool(causal)), float(scale),
                                    _ref(tensor4(dq_acc, "dq_acc", d)), _ref(tensor4(dk_acc, "dk_acc", d)),
                                    _ref(tensor4(dv_acc, "dv_acc", d)), _ptr(_workspace(workspace, d)),
-                                   workspace.numel(), _stream(q)))
+                                   workspace.numel(), RING_BWD_REUSE_WORKSPACE if reuse_workspace else 0,
+                                   _stream(q)))
     return dq_acc, dk_acc, dv_acc
 
 

@@ -63,6 +63,7 @@ def ring_backward(q_rot, k_shards, v_shards, o, lse, dout, shard_order, shard_le
         need = lwm.lwm_blockattn_bwd_workspace_size(B, H, Lq, shard_len, D)
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     last_q = q_offset + Lq - 1
+    first = True  # the first visited shard writes the block's delta and rescaled lse; the rest reuse them
     for j in shard_order:
         if causal and j * shard_len > last_q:
             continue
@@ -73,7 +74,9 @@ def ring_backward(q_rot, k_shards, v_shards, o, lse, dout, shard_order, shard_le
             dv_acc[j] = torch.zeros(kj.shape, dtype=torch.float32, device=dev)
         lwm.lwm_ring_step_bwd(q_rot, kj, v_shards[j], o, lse, dout, dq_acc, dk_acc[j], dv_acc[j], seg_q=seg_q,
                               seg_k=None if seg_k_shards is None else seg_k_shards[j], q_offset=q_offset,
-                              k_offset=j * shard_len, causal=causal, scale=scale, workspace=workspace)
+                              k_offset=j * shard_len, causal=causal, scale=scale, workspace=workspace,
+                              reuse_workspace=not first)
+        first = False
     return dq_acc, dk_acc, dv_acc
 
 

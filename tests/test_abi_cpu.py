@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol():
     assert set(names) == set(lwm.EXPORTS), names
     for n in names:
         assert hasattr(L, n), n
-    assert L.lwm_abi_version() == 5
+    assert L.lwm_abi_version() == 6
     assert L.lwm_last_error() == b""
 
 
@@ -99,8 +99,8 @@ def test_ring_backward_validation():
     q = t4()
     acc = t4(dtype=1)
     ws = L.lwm_blockattn_bwd_workspace_size(1, 2, 8, 8, 128)
-    args = lambda dqa, dka, dva, lse=16, nbytes=ws: (r(q), r(q), r(q), r(q), lse, r(q), None, None, 0, 0, 1, 0.0,
-                                                    r(dqa), r(dka), r(dva), 256, nbytes, None)
+    args = lambda dqa, dka, dva, lse=16, nbytes=ws, flags=0: (r(q), r(q), r(q), r(q), lse, r(q), None, None, 0, 0, 1,
+                                                             0.0, r(dqa), r(dka), r(dva), 256, nbytes, flags, None)
     st = L.lwm_ring_step_bwd(*args(q, acc, acc))  # bf16 accumulator
     assert st == -1 and "float32" in L.lwm_last_error().decode()
     st = L.lwm_ring_step_bwd(*args(acc, t4(dtype=1, L=9), acc))
@@ -110,7 +110,10 @@ def test_ring_backward_validation():
     st = L.lwm_ring_step_bwd(*args(acc, acc, acc, lse=None))
     assert st == -1 and "lse" in L.lwm_last_error().decode()
     assert L.lwm_ring_step_bwd(r(q), r(q), r(q), r(q), 16, r(q), 16, None, 0, 0, 1, 0.0, r(acc), r(acc), r(acc),
-                               256, ws, None) == -1
+                               256, ws, 0, None) == -1
+    for flags in (2, -1):
+        st = L.lwm_ring_step_bwd(*args(acc, acc, acc, flags=flags))
+        assert st == -1 and "flags" in L.lwm_last_error().decode()
 
 
 def test_rope_validation():

@@ -139,3 +139,36 @@ def test_ring_backward_order_and_accumulation():
     lwm.lwm_ring_step_bwd(q, k[0], v[0], o, lse, do, dq3, z, z.clone(), q_offset=0, k_offset=10 * S)
     torch.cuda.synchronize()
     assert torch.equal(dq3, a[0]) and not bool(z.any())
+
+
+def test_ring_backward_reused_workspace_is_exact():
+    """Later steps of a ring reuse the delta and rescaled lse the first step wrote into the workspace
+    (path.ring_backward does): bit-identical accumulators to recomputing them at every step,
+    including with packing, where the first shard visited is not the first in key order."""
+    need_gpu()
+    note("ring backward: reusing the first step's delta/lse workspace equals recomputing it")
+    for segs in (False, True):
+        n, S, Lq, q_off, H = 5, 96, 96, 4 * 96, 2
+        seed = 2300 + int(segs)
+        q = dev(synth.normal(seed, "q", (1, Lq, H, 128)), "bf16")
+        do = dev(synth.normal(seed, "do", (1, Lq, H, 128)), "bf16")
+        k = [dev(synth.normal(seed, "k", (1, S, H, 128), shard=j), "bf16") for j in range(n)]
+        v = [dev(synth.normal(seed, "v", (1, S, H, 128), shard=j), "bf16") for j in range(n)]
+        seg = synth.random_segment_ids(seed, 1, n * S, 70) if segs else None
+        sq = None if seg is None else seg_dev(seg[:, q_off:q_off + Lq])
+        sk = None if seg is None else [seg_dev(seg[:, j * S:(j + 1) * S]) for j in range(n)]
+        order = [4, 3, 2, 1, 0]
+        o, _, lse = path.ring_forward(q, k, v, order, S, q_off, seg_q=sq, seg_k_shards=sk)
+        dq_r, dk_r, dv_r = path.ring_backward(q, k, v, o, lse, do, order, S, q_off, seg_q=sq, seg_k_shards=sk)
+        dq_f = torch.zeros_like(dq_r)
+        ws = torch.empty(lwm.lwm_blockattn_bwd_workspace_size(1, H, Lq, S, 128), dtype=torch.uint8, device="cuda")
+        for j in order:
+            dkj = torch.zeros((1, S, H, 128), dtype=torch.float32, device="cuda")
+            dvj = torch.zeros_like(dkj)
+            lwm.lwm_ring_step_bwd(q, k[j], v[j], o, lse, do, dq_f, dkj, dvj, seg_q=sq,
+                                  seg_k=None if sk is None else sk[j], q_offset=q_off, k_offset=j * S, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(dkj, dk_r[j]) and torch.equal(dvj, dv_r[j]), (segs, j)
+        assert torch.equal(dq_f, dq_r), segs
+    with pytest.raises(ValueError, match="reuse_workspace"):
+        lwm.lwm_ring_step_bwd(q, k[0], v[0], o, lse, do, dq_f, dkj, dvj, q_offset=q_off, reuse_workspace=True)
