@@ -47,6 +47,8 @@ def kernel_work(w, name):
         "bwd_dkdv": (8 * D * pairs, 6 * t),
         # the dQ kernel's share of the method's products is dQ (its S and dP are recomputation)
         "bwd_dq": (2 * D * pairs, 5 * t + 2 * lse_bytes),
+        # dQ from the stored dS: reads two bytes of dS per visible pair and K, writes dQ
+        "bwd_dq_ds": (2 * D * pairs, 2 * pairs + 2 * t),
         "bwd_delta": (0, 2 * t + lse_bytes),
         "rope_bf16": (0, 2 * t),
         "rope_f32": (0, 2 * t),
@@ -219,7 +221,7 @@ def bench_extras(torch, lwm, path, workloads, configs, steps=3, warmup=1):
     ms, prof, n, nw = time_settled(packed_train_step, steps, warmup, lwm, torch)
     ks = kernels_table(prof, n)
     tflop = 14 * w.D * w.visible_pairs()
-    bk = sum(ks[k]["ms_per_step"] for k in ("bwd_delta", "bwd_dq", "bwd_dkdv") if k in ks)
+    bk = sum(ks[k]["ms_per_step"] for k in ("bwd_delta", "bwd_dq", "bwd_dq_ds", "bwd_dkdv") if k in ks)
     out[w.name + "_train"] = {"ms_per_step": ms, "tflops": tflop / ms / 1e9,
                               "pct_of_bf16_peak": 100 * tflop / ms / 1e9 / configs.PEAK_BF16_TFLOPS,
                               "attn_bwd_ms": bk, "attn_bwd_tflops": 10 * w.D * w.visible_pairs() / bk / 1e9,
@@ -259,7 +261,7 @@ def bench_extras(torch, lwm, path, workloads, configs, steps=3, warmup=1):
     dq_acc = torch.empty((w.B, S, w.H, w.D), **f32)
     dk_acc = {j: torch.empty((w.B, S, w.H, w.D), **f32) for j in kr}
     dv_acc = {j: torch.empty((w.B, S, w.H, w.D), **f32) for j in kr}
-    ws = torch.empty(lwm.lwm_blockattn_bwd_workspace_size(w.B, w.H, S, S, w.D), dtype=torch.uint8, device="cuda")
+    ws = lwm.bwd_workspace(w.B, w.H, S, S, w.D, "cuda")
 
     def ring_bwd_step():
         for t in (dq_acc, *dk_acc.values(), *dv_acc.values()):
@@ -269,7 +271,7 @@ def bench_extras(torch, lwm, path, workloads, configs, steps=3, warmup=1):
 
     ms, prof, n, nw = time_settled(ring_bwd_step, steps, warmup, lwm, torch)
     ks = kernels_table(prof, n)
-    kms = sum(ks[k]["ms_per_step"] for k in ("bwd_delta", "bwd_dq", "bwd_dkdv") if k in ks)
+    kms = sum(ks[k]["ms_per_step"] for k in ("bwd_delta", "bwd_dq", "bwd_dq_ds", "bwd_dkdv") if k in ks)
     bflop = 10 * w.D * w.visible_pairs()
     out[w.name + "_backward"] = {
         "ms_per_step": ms, "ring_steps_per_pass": ks["bwd_dkdv"]["launches_per_step"],
@@ -370,7 +372,7 @@ def main():
     flop = w.total_flop()
     value = flop / (ms * 1e-3) / 1e12
     fk = kernels["attn_fwd_bf16"]
-    bwd_ms = sum(kernels[k]["ms_per_step"] for k in ("bwd_delta", "bwd_dq", "bwd_dkdv") if k in kernels)
+    bwd_ms = sum(kernels[k]["ms_per_step"] for k in ("bwd_delta", "bwd_dq", "bwd_dq_ds", "bwd_dkdv") if k in kernels)
     result = {
         "metric": METRIC,
         "value": value,
@@ -386,7 +388,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "seq_len": w.Lq, "heads": w.H, "head_dim": w.D,
                    "theta": w.theta, "causal": True, "rope_layout": "half", "fwd_tile": "128 queries x 64 keys",
-                   "bwd_tiles": "dQ: 128 queries x 64 keys; dK/dV: 256 keys x 64 queries"},
+                   "bwd_tiles": "dK/dV: 256 keys x 64 queries, storing dS; dQ from stored dS: 256 queries x 64 keys",
+                   "bwd_ds_heads_per_pass": lwm.default_ds_heads(w.B, w.H, w.Lq, w.Lk, w.D)},
         "pct_of_bf16_peak": 100 * value / configs.PEAK_BF16_TFLOPS,
         "tokens_per_s": w.B * w.Lq / (ms * 1e-3),
         "attention_fwd_tflops": w.fwd_flop() / fk["avg_ms"] / 1e9,

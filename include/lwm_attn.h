@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define LWM_ABI_VERSION 6
+#define LWM_ABI_VERSION 7
 
 typedef enum {
   LWM_OK = 0,
@@ -126,6 +126,18 @@ int lwm_blockattn_fwd(const lwm_tensor4* q, const lwm_tensor4* k, const lwm_tens
 size_t lwm_blockattn_bwd_workspace_size(int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D);
 
 /*
+ * Bytes of workspace with room for the stored-dS backward over heads_per_pass (batch, head)
+ * pairs at a time: lwm_blockattn_bwd_workspace_size() plus heads_per_pass slots of
+ * Lk64 * ldq * 2 bytes, Lk64 = Lk rounded up to 64 and ldq = Lq rounded up to 256 (each slot
+ * holds one pair's dS^T in bf16).  heads_per_pass
+ * is clamped to B * H; the minimum size comes back for heads_per_pass <= 0, empty sizes, or Lq
+ * above 2^21 (no stored-dS path), SIZE_MAX if the size does not fit in a size_t.  How a larger
+ * workspace is used is described at lwm_blockattn_bwd.
+ */
+size_t lwm_blockattn_bwd_workspace_size_ds(int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
+                                           int64_t heads_per_pass);
+
+/*
  * Blockwise attention backward (bf16 only).  The pages train the model with RingAttention at
  * up to a million tokens ("LWM：突破 100 万 Token 的开源大模型", section 概述; the context is grown
  * step by step during training, "[论文解读] World Model on Million-Length Video And Language With
@@ -139,7 +151,13 @@ size_t lwm_blockattn_bwd_workspace_size(int64_t B, int64_t H, int64_t Lq, int64_
  * (not accumulated) and are gradients w.r.t. the operands given (the rotated Q', K'); apply
  * lwm_rope_apply(inverse=1) to dq and dk for gradients w.r.t. the pre-RoPE Q and K.
  * workspace: device memory of at least lwm_blockattn_bwd_workspace_size() bytes, 256-byte
- * aligned; its contents on entry do not matter.  Status: LWM_ERR_INVALID_ARG for NULL or
+ * aligned; its contents on entry do not matter.  When it also holds G >= min(B * H, 8) slots
+ * (lwm_blockattn_bwd_workspace_size_ds), the backward stores dS instead of recomputing it: in
+ * passes over G (batch, head) pairs (a multiple of 8 unless G = B * H), the dK/dV kernel also
+ * writes each pair's dS^T (bf16, as the products use it) into the slots, and dQ = scale dS K
+ * is formed from them, which replaces the recomputation of S and dP for dQ (5 products instead
+ * of 7, plus two bytes of dS per visible pair written and read).  Both paths give the same
+ * results; with less room the recomputing path runs.  Status: LWM_ERR_INVALID_ARG for NULL or
  * misaligned pointers and mismatched shapes, LWM_ERR_UNSUPPORTED for fp32 operands, D != 128 or
  * launch grids beyond 2^31 - 1 workgroups, LWM_ERR_WORKSPACE for a short or misaligned
  * workspace, LWM_ERR_HIP if a launch fails.
@@ -202,8 +220,10 @@ int lwm_ring_step(const lwm_tensor4* q, const lwm_tensor4* k_shard, const lwm_te
  * scale as in lwm_blockattn_fwd.  dq_acc (like q) and dk_acc, dv_acc (like k_shard) are
  * float32 lwm_tensor4 views that are read and added to (the caller zeroes them before the first
  * step); results are w.r.t. the rotated operands, as for lwm_blockattn_bwd.  workspace: at
- * least lwm_blockattn_bwd_workspace_size(B, H, Lq, Lk, D) bytes, 256-byte aligned; the call
- * writes D and the rescaled lse of the query block into it.  Both depend on the query block only,
+ * least lwm_blockattn_bwd_workspace_size(B, H, Lq, Lk, D) bytes, 256-byte aligned (room for
+ * stored dS, sized by lwm_blockattn_bwd_workspace_size_ds with the shard's Lk, is used as in
+ * lwm_blockattn_bwd); the call writes D and the rescaled lse of the query block into it, ahead
+ * of any dS slots.  Both depend on the query block only,
  * so the steps of one ring after the first may pass flags = LWM_RING_BWD_REUSE_WORKSPACE to use
  * what the first step wrote instead of recomputing it (same workspace, and the same q, o, lse,
  * dout and shape as that step; the library cannot check this).  flags: 0 or

@@ -245,6 +245,33 @@ size_t lwm_blockattn_bwd_workspace_size(int64_t B, int64_t H, int64_t Lq, int64_
 
 namespace {
 
+// Stored dS: one (batch, head) pair's dS^T is Lk rounded up to 64 rows of Lq rounded up to 256
+// bf16 values (in blocks of 64 x 64).  The kernels address a workgroup's rows with 32-bit
+// offsets, so rows are at most kMaxDsLd values.
+constexpr int64_t kMaxDsLd = int64_t(1) << 21;
+int64_t ds_row_len(int64_t Lq) { return (Lq + 255) / 256 * 256; }
+size_t ds_slot_bytes(int64_t Lq, int64_t Lk) { return (size_t)((Lk + 63) / 64 * 64) * (size_t)ds_row_len(Lq) * 2; }
+
+}  // namespace
+
+extern "C" {
+
+size_t lwm_blockattn_bwd_workspace_size_ds(int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
+                                           int64_t heads_per_pass) {
+  const size_t base = lwm_blockattn_bwd_workspace_size(B, H, Lq, Lk, D);
+  if (B <= 0 || H <= 0 || Lq <= 0 || Lk <= 0 || heads_per_pass <= 0) return base;
+  const int64_t ld = ds_row_len(Lq);
+  if (ld > kMaxDsLd || Lk > (int64_t(1) << 31)) return base;
+  const size_t slot = ds_slot_bytes(Lq, Lk);
+  const size_t heads = (size_t)(heads_per_pass < B * H ? heads_per_pass : B * H);
+  if (heads > (SIZE_MAX - base) / slot) return SIZE_MAX;
+  return base + heads * slot;
+}
+
+}  // extern "C"
+
+namespace {
+
 // Checks shared by the backward and the backward ring step; fills every parameter but the
 // gradient outputs.
 int prepare_bwd(const lwm_tensor4* q, const lwm_tensor4* k, const lwm_tensor4* v, const lwm_tensor4* o,
@@ -274,6 +301,21 @@ int prepare_bwd(const lwm_tensor4* q, const lwm_tensor4* k, const lwm_tensor4* v
   p->lse = lse;
   p->delta = static_cast<float*>(workspace);
   p->lse2 = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) + need / 2) : nullptr;
+  // Room after the two rows for the stored dS^T of at least min(B*H, 8) (batch, head) pairs: the
+  // dK/dV kernel writes dS and dQ is formed from it.  Passes take whole multiples of 8 pairs (one
+  // per XCD) unless every pair fits in one.
+  if (!empty && workspace && q->L > 0 && k->L > 0 && ds_row_len(q->L) <= kMaxDsLd) {
+    const int64_t ld = ds_row_len(q->L), BH = q->B * q->H;
+    const size_t slot = ds_slot_bytes(q->L, k->L);
+    const size_t room = (workspace_bytes - need) / slot;
+    int64_t g = room < (size_t)BH ? (int64_t)room : BH;
+    if (g < BH && g >= 8) g &= ~int64_t(7);
+    if (g >= (BH < 8 ? BH : 8)) {
+      p->ds = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + need);
+      p->ds_ld = ld;
+      p->ds_heads = (int)g;
+    }
+  }
   p->B = (int)q->B; p->H = (int)q->H; p->Lq = (int)q->L; p->Lk = (int)k->L;
   p->seg_q = seg_q; p->seg_k = seg_k;
   p->q_offset = q_offset; p->k_offset = k_offset; p->causal = causal;
@@ -364,8 +406,10 @@ int lwm_blockattn_bwd_noalloc(const lwm_tensor4* q, const lwm_tensor4* k, const 
   void* ws = nullptr;
   int s;
   if ((s = static_scratch(&ws))) return s;
+  // exactly the two rows per query: the static array has no room for stored dS
+  const size_t bytes = q ? lwm_blockattn_bwd_workspace_size(q->B, q->H, q->L, 0, q->D) : kStaticBwdBytes;
   return lwm_blockattn_bwd(q, k, v, o, lse, dout, seg_q, seg_k, q_offset, k_offset, causal, scale, dq, dk, dv, ws,
-                           kStaticBwdBytes, stream);
+                           bytes, stream);
 }
 
 int lwm_blockattn_bwd_rope(const lwm_tensor4* q_rot, const lwm_tensor4* k_rot, const lwm_tensor4* v,

@@ -24,6 +24,7 @@
 //  S and dP in both kernels costs two extra products over the five the method needs; in exchange
 //  no partial dQ is ever written to or reduced through memory.
 
+#include <cstddef>
 #include <type_traits>
 
 #include "attn_common.hpp"
@@ -64,6 +65,27 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
 }
 
 // ------------------------------------------------------------------------------ dQ
+// A wave's dQ^T accumulator (query rows wr0 + lane, features in the accumulator rows) out to
+// memory: added into dq_acc (backward ring step, float32), or rotated back when RoPE is fused and
+// rounded once to bf16.  Every wave of the workgroup calls it (the row helpers have block-wide
+// barriers); `stage_w` is 16 KB of LDS of the wave's own, free by then.
+__device__ __forceinline__ void dq_epilogue(const BwdParams& p, uint8_t* stage_w, f32x16 (&acc)[4], int b, int hh,
+                                            int wr0, int h32, bool segs) {
+  const int rows_valid = max(0, min(32, p.Lq - wr0));
+  if (p.dq_acc) {  // backward ring step: dQ += this shard's share, in float32
+    add_rows_f32(stage_w, acc, p.scale, p.dq_acc + b * p.sdqa.b + hh * p.sdqa.h + wr0 * p.sdqa.l, p.sdqa.l,
+                 rows_valid);
+  } else {
+    if (p.rope.on) {  // dQ' -> dQ (inverse RoPE of the query rows) before the one rounding to bf16
+      const bool restart = segs && p.rope.restart;
+      const int64_t pos = rope_row_position(restart ? p.seg_q + (int64_t)b * p.Lq : nullptr, p.Lq, wr0, restart,
+                                            p.rope.q_pos_offset);
+      rope_unrotate_acc(acc, pos, p.rope, h32);
+    }
+    store_rows_bf16(stage_w, acc, p.scale, p.dq + b * p.sdq.b + hh * p.sdq.h + wr0 * p.sdq.l, p.sdq.l, rows_valid);
+  }
+}
+
 struct SmemDq {
   uint8_t kv[2][2][kTileBytes];  // [stage][K, V] row-major swizzled
   int32_t seg[2][64];
@@ -76,9 +98,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c32 = lane & 31, h32 = lane >> 5;
   const int nqt = (p.Lq + BM - 1) / BM;
-  int bh, qt;
+  int lbh, qt;
   const bool segs = p.seg_q != nullptr;
-  map_block(blockIdx.x, nqt, p.B * p.H, true, segs, bh, qt);
+  map_block(blockIdx.x, nqt, p.bh_count, true, segs, lbh, qt);
+  const int bh = p.bh0 + lbh;
   const int b = bh / p.H, hh = bh - b * p.H;
   const int q0 = qt * BM;
   const int qlast = min(q0 + BM, p.Lq) - 1;
@@ -255,24 +278,231 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
   };
   for (int it = 0; it < ntiles; ++it) tile(it & 1, it);
   __syncthreads();
-  const int rows_valid = max(0, min(32, p.Lq - wr0));
-  if (p.dq_acc) {  // backward ring step: dQ += this shard's share, in float32
-    uint8_t* stage_w = reinterpret_cast<uint8_t*>(&sm) + w * (32 * D * 4);
-    add_rows_f32(stage_w, acc, p.scale, p.dq_acc + b * p.sdqa.b + hh * p.sdqa.h + wr0 * p.sdqa.l, p.sdqa.l,
-                 rows_valid);
-  } else {
-    if (p.rope.on) {  // dQ' -> dQ (inverse RoPE of the query rows) before the one rounding to bf16
-      const bool restart = segs && p.rope.restart;
-      const int64_t pos = rope_row_position(restart ? p.seg_q + (int64_t)b * p.Lq : nullptr, p.Lq, wr0, restart,
-                                            p.rope.q_pos_offset);
-      rope_unrotate_acc(acc, pos, p.rope, h32);
+  dq_epilogue(p, reinterpret_cast<uint8_t*>(&sm) + w * (32 * D * 4), acc, b, hh, wr0, h32, segs);
+}
+
+// ------------------------------------------------------------------------------ dQ from stored dS
+// When the dK/dV kernel has stored dS^T, dQ^T = scale K^T dS^T is one product over data already
+// computed: a workgroup of 8 waves per 256-query tile walks the visible 64-key tiles, bringing
+// the K tile and the matching 64 x 256 block of dS^T (rows = keys, queries along the row) into
+// LDS by direct loads through a three-stage ring, two tiles ahead.  Both operands come out of LDS
+// by transposing reads: K^T as in the dQ kernel above, and wave w's 32 queries of dS^T in the key
+// order of a 32x32 accumulator's lane half.  The stored block holds dS for every pair the dK/dV
+// kernel visited (zero where masked), not for pairs outside its ranges, so on tiles that need the
+// mask every invisible pair is cleared before the product.  HBM-bound: two bytes of dS per
+// visible pair are read once.
+constexpr int kDsWaves = 8;
+constexpr int kDsQueries = kDsWaves * 32;  // queries per workgroup
+// Stored dS^T of one (batch, head) pair: blocks of 64 keys x 64 queries (8 KB), key block after
+// key block, each the ds_ld / 64 query blocks in order, so the dK/dV kernel writes whole blocks
+// per query tile and this kernel reads 32 KB in a row per key tile (plain rows of dS^T would
+// scatter every write over as many rows).  Inside a block, 16-byte chunk j (queries 8j .. 8j + 7)
+// of key r sits at byte j * 1024 + r * 16: one lane of the dK/dV kernel holds exactly such a chunk
+// for its key (its LDS query rows are permuted by swap23 for that), so each of its stores is a
+// whole 16-byte fragment and 32 lanes write 512 contiguous bytes.
+constexpr int kDsBlock = 64;
+constexpr int kDsBlockBytes = kDsBlock * kDsBlock * 2;
+constexpr int kDsChunkBytes = kDsBlock * 16;  // one chunk of all 64 keys of a block
+__device__ __forceinline__ int64_t ds_slot_bytes(const BwdParams& p) {
+  return (int64_t)((p.Lk + kDsBlock - 1) / kDsBlock) * (p.ds_ld / kDsBlock) * kDsBlockBytes;
+}
+struct StageDs {
+  uint8_t k[kTileBytes];                 // K rows, row-major swizzled
+  uint8_t s[64 * kDsQueries * 2];        // dS^T rows (64 keys x 256 queries), 512 bytes per key
+  int32_t seg[64];
+};
+template <int S>
+using DsStage = std::integral_constant<int, S>;
+
+__global__ __launch_bounds__(kDsWaves * kWave) void bwd_dq_ds_kernel(BwdParams p) {
+  constexpr int MW = 32, BM = kDsQueries, BN = 64;
+  __shared__ __attribute__((aligned(1024))) StageDs lds_s0;
+  __shared__ __attribute__((aligned(1024))) StageDs lds_s1;
+  __shared__ __attribute__((aligned(1024))) StageDs lds_s2;
+  auto stage = [&](auto sc) __attribute__((always_inline)) -> StageDs& {
+    if constexpr (decltype(sc)::value == 0) return lds_s0;
+    else if constexpr (decltype(sc)::value == 1) return lds_s1;
+    else return lds_s2;
+  };
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c32 = lane & 31, h32 = lane >> 5;
+  const int nqt = (p.Lq + BM - 1) / BM;
+  int lbh, qt;
+  const bool segs = p.seg_q != nullptr;
+  map_block(blockIdx.x, nqt, p.bh_count, true, segs, lbh, qt);
+  const int bh = p.bh0 + lbh;
+  const int b = bh / p.H, hh = bh - b * p.H;
+  const int q0 = qt * BM;
+  const int qlast = min(q0 + BM, p.Lq) - 1;
+  const int wr0 = q0 + w * MW, wr1 = min(wr0 + MW, p.Lq) - 1;
+  const bool wave_rows = wr1 >= wr0;
+  const int64_t gq = p.q_offset + wr0 + c32;
+
+  int kbeg = 0, kend = p.Lk;
+  if (p.causal) kend = (int)imax64(0, imin64(kend, p.q_offset + qlast - p.k_offset + 1));
+  if (segs) {
+    const int32_t* segk = p.seg_k + (int64_t)b * p.Lk;
+    if (causal_self_segments(p.seg_q, p.seg_k, p.Lq, p.Lk, p.q_offset, p.k_offset, p.causal)) {
+      kbeg = max(kbeg, wave_lower_bound(segk, p.Lk, segk[q0]));
+    } else {
+      int lo, hi;
+      segment_range(segk, p.Lk, p.seg_q[(int64_t)b * p.Lq + q0], p.seg_q[(int64_t)b * p.Lq + qlast], lo, hi);
+      kbeg = max(kbeg, lo);
+      kend = min(kend, hi);
     }
-    uint8_t* stage_w = reinterpret_cast<uint8_t*>(&sm) + w * (32 * D * 2);
-    store_rows_bf16(stage_w, acc, p.scale, p.dq + b * p.sdq.b + hh * p.sdq.h + wr0 * p.sdq.l, p.sdq.l, rows_valid);
   }
+  const int t_begin = kbeg / BN;
+  const int ntiles = (kend > kbeg) ? (kend + BN - 1) / BN - t_begin : 0;
+  int32_t wseg0 = 0, wseg1 = 0;
+  if (segs && wave_rows) {
+    wseg0 = p.seg_q[(int64_t)b * p.Lq + wr0];
+    wseg1 = p.seg_q[(int64_t)b * p.Lq + wr1];
+  }
+  const int32_t myseg = segs ? p.seg_q[(int64_t)b * p.Lq + min(wr0 + c32, p.Lq - 1)] : 0;
+  f32x16 acc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+
+  const uint8_t* kg = reinterpret_cast<const uint8_t*>(p.k + b * p.sk.b + hh * p.sk.h);
+  const int64_t kl_bytes = p.sk.l * 2;
+  const int64_t k_extent = (int64_t)(p.Lk - 1) * kl_bytes + 256;
+  // this pair's dS^T blocks (see ds_block_row): the tile of keys k0.. is the four blocks of
+  // query blocks q0/64 .. + 3 of key block k0/64, 32 KB in a row
+  const uint8_t* sg = reinterpret_cast<const uint8_t*>(p.ds) + (int64_t)lbh * ds_slot_bytes(p) +
+                      (int64_t)(q0 / kDsBlock) * kDsBlockBytes;
+  const int64_t ds_row_bytes = p.ds_ld / kDsBlock * kDsBlockBytes;  // one key block's row of blocks
+  const int32_t* segk_row = segs ? p.seg_k + (int64_t)b * p.Lk : nullptr;
+  // K tile: 16 blocks of 1 KB, two per wave; dS^T tile: 32 blocks of 1 KB, four per wave.  In
+  // LDS the dS^T tile is two row-major swizzled 64 x 128 tiles side by side (queries 0..127 and
+  // 128..255 of the workgroup): 16-byte chunk c of row r of half hr is chunk c % 8 of key r in
+  // query block 2 hr + c / 8
+  int ld_voff_k[2], ld_voff_s[4];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int row = (w * 2 + r) * 4 + (lane >> 4);
+    ld_voff_k[r] = (int)(row * kl_bytes) + (((lane & 15) ^ swz16(row)) << 4);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int blk = w * 4 + r, hr = blk >> 4, row = (blk & 15) * 4 + (lane >> 4);
+    const int c = (lane & 15) ^ swz16(row);
+    ld_voff_s[r] = (2 * hr + (c >> 3)) * kDsBlockBytes + (c & 7) * kDsChunkBytes + row * 16;
+  }
+  auto issue = [&](int tile, StageDs& dst) __attribute__((always_inline)) {
+    const int k0 = tile * BN;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + k0 * kl_bytes, k_extent - k0 * kl_bytes);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(sg + (int64_t)(k0 / kDsBlock) * ds_row_bytes, 4 * kDsBlockBytes);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) load_lds16(rk, &dst.k[(w * 2 + r) * 1024], ld_voff_k[r]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) load_lds16(rs, &dst.s[(w * 4 + r) * 1024], ld_voff_s[r]);
+    if (segs && w == 0) load_lds4(make_rsrc(segk_row + k0, (int64_t)(p.Lk - k0) * 4), &dst.seg[0], lane * 4);
+  };
+  int tlo0, thi0;
+  tr_offsets(lane, 0, tlo0, thi0);
+  // wave w's queries: half-row w / 4, column block w % 4 of it
+  const int s_half = (w >> 2) * 16384;
+  const int tlo_s = tlo0 ^ ((w & 3) << 6), thi_s = thi0 ^ ((w & 3) << 6);
+
+  auto tile = [&](auto sc, int it) __attribute__((always_inline)) {
+    StageDs& cur = stage(sc);
+    const int k0 = (t_begin + it) * BN;
+    // this tile's loads done (the next tile's may still be in flight), then every wave's
+    if (it + 1 < ntiles) {
+      if (segs && w == 0) wait_vmcnt<7>();
+      else wait_vmcnt<6>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    block_barrier();
+    if (it + 2 < ntiles) issue(t_begin + it + 2, stage(DsStage<(decltype(sc)::value + 2) % 3>{}));
+    bool active = wave_rows;
+    bool need_mask = (k0 + BN > p.Lk) || (k0 < kbeg) || (k0 + BN > kend);
+    if (p.causal) {
+      active = active && (p.k_offset + k0 <= p.q_offset + wr1);
+      need_mask = need_mask || (p.k_offset + k0 + BN - 1 > p.q_offset + wr0);
+    }
+    if (segs) {
+      const int32_t ts0 = cur.seg[0], ts1 = cur.seg[min(BN, p.Lk - k0) - 1];
+      active = active && !(ts1 < wseg0 || ts0 > wseg1);
+      need_mask = need_mask || !(ts0 == ts1 && wseg0 == wseg1 && ts0 == wseg0);
+    }
+    if (!active) return;
+
+    // dS^T operand of 16-key group g: keys 16g + 8(e/4) + 4*h32 + e%4 (element e) of query c32
+    bf16x8 dsb[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) dsb[g] = read_xt(cur.s + s_half + g * 4096, tlo_s, thi_s);
+    if (need_mask) {
+      // key kl = 32 kb + 8 g4 + 4 h32 + j is visible iff kl < lim (end of the keys, causal limit)
+      // and its segment is this lane's query's; element 4 (g4 & 1) + j of dsb[2 kb + g4 / 2]
+      int64_t lim64 = (int64_t)p.Lk - k0;
+      if (p.causal) lim64 = imin64(lim64, gq - p.k_offset - k0 + 1);
+      const int limt = (int)imax64(imin64(lim64, BN), 0);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int lim = limt - kb * 32 - 4 * h32;
+        const int32_t* segt = &cur.seg[kb * 32 + 4 * h32];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          u32x4 x = __builtin_bit_cast(u32x4, dsb[2 * kb + u]);
+#pragma unroll
+          for (int eh = 0; eh < 2; ++eh) {
+            const int g4 = 2 * u + eh;
+            i32x4 ks = {myseg, myseg, myseg, myseg};
+            if (segs) ks = *reinterpret_cast<const i32x4*>(segt + 8 * g4);
+            bool vis[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) vis[j] = (8 * g4 + j < lim) & (ks[j] == myseg);
+            x[2 * eh] &= (vis[0] ? 0xFFFFu : 0u) | (vis[1] ? 0xFFFF0000u : 0u);
+            x[2 * eh + 1] &= (vis[2] ? 0xFFFFu : 0u) | (vis[3] ? 0xFFFF0000u : 0u);
+          }
+          dsb[2 * kb + u] = __builtin_bit_cast(bf16x8, x);
+        }
+      }
+    }
+    // dQ^T += K^T dS^T (K^T operands by transposing reads, two ahead)
+    {
+      bf16x8 kf[3];
+      auto kread = [&](int n) {
+        return read_xt(cur.k + (n >> 2) * 4096, tlo0 ^ ((n & 3) << 6), thi0 ^ ((n & 3) << 6));
+      };
+      kf[0] = kread(0);
+      kf[1] = kread(1);
+#pragma unroll
+      for (int n = 0; n < 16; ++n) {  // n = 16-key group * 4 + feature block
+        if (n + 2 < 16) kf[(n + 2) % 3] = kread(n + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        acc[n & 3] = mfma_32x32x16(kf[n % 3], dsb[n >> 2], acc[n & 3]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  if (ntiles > 0) issue(t_begin, lds_s0);
+  if (ntiles > 1) issue(t_begin + 1, lds_s1);
+  int it = 0;
+  for (; it + 3 <= ntiles; it += 3) {
+    tile(DsStage<0>{}, it);
+    tile(DsStage<1>{}, it + 1);
+    tile(DsStage<2>{}, it + 2);
+  }
+  if (it < ntiles) tile(DsStage<0>{}, it);
+  if (it + 1 < ntiles) tile(DsStage<1>{}, it + 1);
+  __syncthreads();
+  // staging for the epilogue: 16 KB per wave, three waves to a stage object
+  StageDs& st = w < 3 ? lds_s0 : (w < 6 ? lds_s1 : lds_s2);
+  dq_epilogue(p, reinterpret_cast<uint8_t*>(&st) + (w % 3) * 16384, acc, b, hh, wr0, h32, segs);
 }
 
 // ------------------------------------------------------------------------------ dK / dV
+// swap23 exchanges bits 2 and 3 of an index: the dK/dV kernel keeps query t of a tile in LDS row
+// swap23(t) of its Q and dO tiles (the per-query rows stay in query order).  Lane half h of a 32 x 32 accumulator holds
+// rows 16u + 4h + {0..3} and 16u + 8 + 4h + {0..3} in operand u, which are then queries
+// 16u + 8h + {0..7}: eight consecutive queries, one 16-byte piece of a stored dS^T row.  Sums over
+// queries are unchanged up to their order, and both dK/dV variants use the same order.
+__device__ __forceinline__ int swap23(int x) { return (x & ~12) | ((x >> 1) & 4) | ((x << 1) & 8); }
 // A workgroup owns 256 keys and has 8 waves, two per SIMD: wave w owns the 32 keys k0 + 32 w.  It
 // keeps their dK^T and dV^T accumulators (128 registers) and their K rows as MFMA operands (32
 // registers) for the whole pass; their V rows sit in LDS.  All eight waves walk the visible
@@ -297,6 +527,9 @@ struct StageQO {
   float dlt[64];
   int32_t seg[64];
 };
+static_assert(offsetof(StageQO, dlt) == offsetof(StageQO, lse2) + 256 &&
+                  offsetof(StageQO, seg) == offsetof(StageQO, lse2) + 512,
+              "the three query-row arrays are consecutive");
 constexpr int kVBytes = BKV * 256;  // V rows of the workgroup's keys, 8 KB per wave
 // after the loop each wave stages its bf16 output rows (8 KB) in its own V rows
 static_assert(kVBytes == kDkdvWaves * 32 * D * 2, "a wave's bf16 staging rows fill its V rows");
@@ -304,6 +537,9 @@ static_assert(kVBytes == kDkdvWaves * 32 * D * 2, "a wave's bf16 staging rows fi
 template <int S>
 using StageC = std::integral_constant<int, S>;
 
+// kStoreDs: also write dS^T of every visited (key, query) sub-tile to the stored-dS matrix (bf16,
+// zero where masked), for bwd_dq_ds_kernel.
+template <bool kStoreDs>
 __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) StageQO lds_qo0;
   __shared__ __attribute__((aligned(1024))) StageQO lds_qo1;
@@ -315,15 +551,28 @@ __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams 
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c32 = lane & 31, h32 = lane >> 5;
   const int nkt = (p.Lk + BKV - 1) / BKV;
-  int bh, kt;
+  int lbh, kt;
   const bool segs = p.seg_q != nullptr;
-  map_block(blockIdx.x, nkt, p.B * p.H, false, segs, bh, kt);
+  map_block(blockIdx.x, nkt, p.bh_count, false, segs, lbh, kt);
+  const int bh = p.bh0 + lbh;
   const int b = bh / p.H, hh = bh - b * p.H;
   const int k0 = kt * BKV;
   const int klast = min(k0 + BKV, p.Lk) - 1;
   const int wk0 = k0 + w * 32, wk1 = min(wk0 + 32, p.Lk) - 1;
   const bool wave_keys = wk1 >= wk0;
   const int krow = wk0 + c32;
+  // stored dS^T: the rows of blocks of this workgroup's four key blocks (those past the pair's
+  // last key block fall outside the resource and their stores are dropped).  Lane (c32, h32)
+  // writes key w*32 + c32 of them, chunks 2u + h32 of a sub-tile.
+  __amdgpu_buffer_rsrc_t rds;
+  int ds_wave = 0;  // the wave's part of the store offsets (its keys' block and rows); wave-uniform
+  if constexpr (kStoreDs) {
+    const int64_t row_bytes = p.ds_ld / kDsBlock * kDsBlockBytes;
+    const int kb0 = k0 / kDsBlock, nkb = (p.Lk + kDsBlock - 1) / kDsBlock;
+    rds = make_rsrc(reinterpret_cast<const uint8_t*>(p.ds) + (int64_t)lbh * ds_slot_bytes(p) + kb0 * row_bytes,
+                    (int64_t)(nkb - kb0) * row_bytes);
+    ds_wave = (w >> 1) * (int)row_bytes + (w & 1) * 32 * 16;
+  }
 
   // this wave's 32 V rows into its 8 KB of LDS (8 blocks of 1 KB; rows past the end read as zero),
   // in flight during the query-range search; only this wave reads them
@@ -381,7 +630,7 @@ __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams 
   // some key of the wave and some query at or after the wave's first key, which bounds it to
   // (-2^30, 2^30 + 32) there; clamping outside that range changes no mask
   const int kq = (int)imax64(-(int64_t(1) << 30), imin64((int64_t(1) << 30) + 64, p.k_offset - p.q_offset));
-  const int krh = krow - 4 * h32;  // this lane's key less the first query row it holds in a tile
+  const int krh = krow - 8 * h32;  // this lane's key less the first query it holds in a sub-tile
 
   f32x16 dk[4], dv[4];
 #pragma unroll
@@ -397,11 +646,12 @@ __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams 
   const float* dlt_row = p.delta + ((int64_t)b * p.H + hh) * p.Lq;
   const int32_t* segq_row = segs ? p.seg_q + (int64_t)b * p.Lq : nullptr;
   // per q-tile: 16 blocks of 1 KB for Q and 16 for dO, two of each per wave
+  // (LDS row r holds query swap23(r) of the tile)
   const int ld_row0 = w * 8 + (lane >> 4), ld_row1 = ld_row0 + 4;
-  const int ld_voff_q0 = (int)(ld_row0 * ql_bytes) + (((lane & 15) ^ swz16(ld_row0)) << 4);
-  const int ld_voff_q1 = (int)(ld_row1 * ql_bytes) + (((lane & 15) ^ swz16(ld_row1)) << 4);
-  const int ld_voff_o0 = (int)(ld_row0 * ol_bytes) + (((lane & 15) ^ swz16(ld_row0)) << 4);
-  const int ld_voff_o1 = (int)(ld_row1 * ol_bytes) + (((lane & 15) ^ swz16(ld_row1)) << 4);
+  const int ld_voff_q0 = (int)(swap23(ld_row0) * ql_bytes) + (((lane & 15) ^ swz16(ld_row0)) << 4);
+  const int ld_voff_q1 = (int)(swap23(ld_row1) * ql_bytes) + (((lane & 15) ^ swz16(ld_row1)) << 4);
+  const int ld_voff_o0 = (int)(swap23(ld_row0) * ol_bytes) + (((lane & 15) ^ swz16(ld_row0)) << 4);
+  const int ld_voff_o1 = (int)(swap23(ld_row1) * ol_bytes) + (((lane & 15) ^ swz16(ld_row1)) << 4);
   auto issue = [&](int tile, StageQO& dst) __attribute__((always_inline)) {
     const int q0 = tile * BQT;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(qg + q0 * ql_bytes, q_extent - q0 * ql_bytes);
@@ -410,10 +660,16 @@ __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams 
     load_lds16(rq, &dst.q[(2 * w + 1) * 1024], ld_voff_q1);
     load_lds16(ro, &dst.o[(2 * w) * 1024], ld_voff_o0);
     load_lds16(ro, &dst.o[(2 * w + 1) * 1024], ld_voff_o1);
+    // the query rows, one 4-byte load per wave and no branch: wave 0 lse2, wave 1 delta, the
+    // others the segment ids (each the same bytes; without segment ids, lse2 again into the
+    // unused segment slot).  A branch per wave here leaves the compiler unable to tell which
+    // stage the loads in flight write, and it then makes LDS reads of the other stage wait.
     const int64_t rem = (int64_t)(p.Lq - q0) * 4;
-    if (w == 0) load_lds4(make_rsrc(lse2_row + q0, rem), &dst.lse2[0], lane * 4);
-    if (w == 1) load_lds4(make_rsrc(dlt_row + q0, rem), &dst.dlt[0], lane * 4);
-    if (segs && w == 2) load_lds4(make_rsrc(segq_row + q0, rem), &dst.seg[0], lane * 4);
+    const void* row_src = w == 0 ? static_cast<const void*>(lse2_row + q0)
+                                 : (w == 1 ? static_cast<const void*>(dlt_row + q0)
+                                           : (segs ? static_cast<const void*>(segq_row + q0)
+                                                   : static_cast<const void*>(lse2_row + q0)));
+    load_lds4(make_rsrc(row_src, rem), reinterpret_cast<uint8_t*>(&dst.lse2[0]) + min(w, 2) * 256, lane * 4);
   };
   // Row-major operand (Q, dO, V rows; row c32, chunk 2*sd + h32): the XOR swizzle leaves bit 0 of
   // an even chunk index alone, so the offset is a per-lane base plus ((2*sd) ^ swizzle) * 16.
@@ -478,10 +734,11 @@ __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams 
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      // lane owns key krow; element i is query q0 + acc_row(i, h32)
+      // lane owns key krow; element i = 4g + j is LDS row acc_row(i, h32) of the sub-tile, query
+      // q0 + 16(g/2) + 8*h32 + 4(g%2) + j (the per-query rows are kept in query order)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int r4 = BQ * u2 + 8 * g + 4 * h32;
+        const int r4 = BQ * u2 + 16 * (g >> 1) + 4 * (g & 1) + 8 * h32;
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(&cur.lse2[r4]);
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(&cur.dlt[r4]);
 #pragma unroll
@@ -492,26 +749,27 @@ __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams 
         }
       }
       if (need_mask) {
-        // element i holds query ql = 8*(i/4) + 4*h32 + i%4, visible iff q_offset + q0 + ql >=
-        // k_offset + krow (causal), i.e. 8*(i/4) + i%4 >= lo, and its segment matches this lane's
-        // key; masked scores get exponent -inf (a select).  lo stays in 32 bits: a tile needing the
-        // causal mask has kq + krow - q0 in (-2^31 + 32, 63)
+        // element i = 4g + j holds LDS row 8g + 4*h32 + j, query ql = 16(g/2) + 8*h32 + 4(g%2) + j,
+        // visible iff q_offset + q0 + ql >= k_offset + krow (causal), i.e.
+        // 16(g/2) + 4(g%2) + j >= lo, and its segment matches this lane's key; masked scores get
+        // exponent -inf (a select).  lo stays in 32 bits: a tile needing the causal mask has
+        // kq + krow - q0 in (-2^31 + 32, 63)
         const int lo = p.causal ? kq + (krh - q0) : -BQ;
-        // the segment ids of this lane's rows, all four groups read under one branch; the lane half's
-        // offset 4 * h32 comes from threadIdx.x itself (a value kept for the loop was spilled)
+        // the segment ids of this lane's queries, all four groups read under one branch; the lane
+        // half's offset 8 * h32 comes from threadIdx.x itself (a value kept for the loop was spilled)
         i32x4 qs[4];
 #pragma unroll
         for (int g = 0; g < 4; ++g) qs[g] = i32x4{myseg, myseg, myseg, myseg};
         if (segs) {
-          const int32_t* segt = &cur.seg[BQ * u2] + ((threadIdx.x >> 3) & 4);
+          const int32_t* segt = &cur.seg[BQ * u2] + ((threadIdx.x >> 2) & 8);
 #pragma unroll
-          for (int g = 0; g < 4; ++g) qs[g] = *reinterpret_cast<const i32x4*>(segt + 8 * g);
+          for (int g = 0; g < 4; ++g) qs[g] = *reinterpret_cast<const i32x4*>(segt + 16 * (g >> 1) + 4 * (g & 1));
         }
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const bool vis = (8 * g + j >= lo) & (qs[g][j] == myseg);
+            const bool vis = (16 * (g >> 1) + 4 * (g & 1) + j >= lo) & (qs[g][j] == myseg);
             s[4 * g + j] = vis ? s[4 * g + j] : -INFINITY;
           }
         }
@@ -523,6 +781,19 @@ __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams 
       }
       const bf16x8 pb[2] = {pack8(s, 0), pack8(s, 1)};
       const bf16x8 dsb[2] = {pack8(dp, 0), pack8(dp, 1)};
+      if constexpr (kStoreDs) {
+        // dsb[u] holds queries q0 + 16u + 8*h32 + 0..7: chunk (q0 % 64) / 8 + 2u + h32 of this
+        // lane's key in the stored layout
+        // the lane's part (row c32, chunk + h32) comes from threadIdx.x itself: a value kept for the
+        // loop is spilled, and its reload would wait for the next tile's loads
+        const int tx = (int)threadIdx.x;
+        const int off = ds_wave + (q0 / kDsBlock) * kDsBlockBytes + ((q0 % kDsBlock) / 8) * kDsChunkBytes +
+                        ((tx & 31) << 4) + ((tx & 32) << 5);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, dsb[u]), rds, off + 2 * u * kDsChunkBytes,
+                                                 0, 0);
+      }
       // dV^T += dO^T P, dK^T += Q^T dS (transposed operands by transposing reads, one step ahead)
       {
         bf16x8 g[2][2];
@@ -593,19 +864,35 @@ __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams 
 
 }  // namespace
 
-hipError_t launch_attn_bwd(const BwdParams& p, hipStream_t stream) {
-  if (p.B == 0 || p.H == 0) return hipSuccess;
+hipError_t launch_attn_bwd(const BwdParams& params, hipStream_t stream) {
+  if (params.B == 0 || params.H == 0) return hipSuccess;
+  BwdParams p = params;
+  const int BH = p.B * p.H;
+  if (p.Lq > 0 && !p.delta_ready) {
+    const int64_t rows = (int64_t)BH * p.Lq;
+    LWM_LAUNCH("bwd_delta", bwd_delta_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), stream, p);
+  }
+  const int nkt = (p.Lk + BKV - 1) / BKV;
+  if (p.ds && p.Lq > 0 && p.Lk > 0) {
+    // stored dS: per pass of ds_heads (batch, head) pairs, dK/dV (writing dS^T), then dQ from it
+    const int nqt = (p.Lq + kDsQueries - 1) / kDsQueries;
+    for (int bh0 = 0; bh0 < BH; bh0 += p.ds_heads) {
+      p.bh0 = bh0;
+      p.bh_count = min(p.ds_heads, BH - bh0);
+      LWM_LAUNCH("bwd_dkdv", bwd_dkdv_kernel<true>, dim3(nkt * p.bh_count), dim3(kDkdvWaves * kWave), stream, p);
+      LWM_LAUNCH("bwd_dq_ds", bwd_dq_ds_kernel, dim3(nqt * p.bh_count), dim3(kDsWaves * kWave), stream, p);
+    }
+    return hipGetLastError();
+  }
+  p.ds = nullptr;
+  p.bh0 = 0;
+  p.bh_count = BH;
   if (p.Lq > 0) {
-    const int64_t rows = (int64_t)p.B * p.Lq * p.H;
-    if (!p.delta_ready)
-      LWM_LAUNCH("bwd_delta", bwd_delta_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), stream, p);
     const int nqt = (p.Lq + 127) / 128;
-    LWM_LAUNCH("bwd_dq", bwd_dq_kernel, dim3(nqt * p.B * p.H), dim3(kThreads), stream, p);
+    LWM_LAUNCH("bwd_dq", bwd_dq_kernel, dim3(nqt * BH), dim3(kThreads), stream, p);
   }
-  if (p.Lk > 0) {
-    const int nkt = (p.Lk + BKV - 1) / BKV;
-    LWM_LAUNCH("bwd_dkdv", bwd_dkdv_kernel, dim3(nkt * p.B * p.H), dim3(kDkdvWaves * kWave), stream, p);
-  }
+  if (p.Lk > 0)
+    LWM_LAUNCH("bwd_dkdv", bwd_dkdv_kernel<false>, dim3(nkt * BH), dim3(kDkdvWaves * kWave), stream, p);
   return hipGetLastError();
 }
 

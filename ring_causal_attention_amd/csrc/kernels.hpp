@@ -98,6 +98,15 @@ struct BwdParams {
   // rope.on: dq and dk are rotated back (inverse RoPE) before they are stored, so they are
   // gradients w.r.t. the pre-RoPE Q and K (stored outputs only, not the ring accumulators)
   RopeFuse rope;
+  // Stored dS (ds != nullptr): the (batch, head) pairs go through in passes of ds_heads; in each
+  // pass the dK/dV kernel also writes dS^T (bf16) of pair bh0 + j into slot j (Lk rounded up to
+  // 64 rows of ds_ld = Lq rounded up to 256 values, in 64 x 64 blocks), and a dQ kernel then
+  // forms dQ from it and K alone instead of recomputing S and dP.
+  uint16_t* ds;
+  int64_t ds_ld;
+  int ds_heads;
+  // the (batch, head) pairs one launch covers: bh0 .. bh0 + bh_count - 1 (set by launch_attn_bwd)
+  int bh0, bh_count;
 };
 
 // Blockwise feed-forward block (bf16): y = (silu(x W_gate^T) * (x W_up^T)) W_down^T over chunks

@@ -40,7 +40,7 @@ class RopeArgs(ctypes.Structure):
 
 _lib = None
 EXPORTS = ["lwm_abi_version", "lwm_last_error", "lwm_rope_apply", "lwm_blockattn_fwd",
-           "lwm_blockattn_bwd_workspace_size", "lwm_blockattn_bwd", "lwm_blockattn_bwd_noalloc", "lwm_blockattn_fwd_rope",
+           "lwm_blockattn_bwd_workspace_size", "lwm_blockattn_bwd_workspace_size_ds", "lwm_blockattn_bwd", "lwm_blockattn_bwd_noalloc", "lwm_blockattn_fwd_rope",
            "lwm_blockattn_bwd_rope", "lwm_ring_step", "lwm_ring_step_bwd",
            "lwm_blockwise_ffn_workspace_size", "lwm_blockwise_ffn", "lwm_profile_enable", "lwm_profile_reset", "lwm_profile_count", "lwm_profile_get",
            "lwm_probe_mfma_bf16"]
@@ -66,6 +66,8 @@ def lib() -> ctypes.CDLL:
     L.lwm_blockattn_fwd.argtypes = [P, P, P, VP, VP, I64, I64, I32, F32, P, VP, VP]
     L.lwm_blockattn_bwd_workspace_size.restype = ctypes.c_size_t
     L.lwm_blockattn_bwd_workspace_size.argtypes = [I64, I64, I64, I64, I64]
+    L.lwm_blockattn_bwd_workspace_size_ds.restype = ctypes.c_size_t
+    L.lwm_blockattn_bwd_workspace_size_ds.argtypes = [I64, I64, I64, I64, I64, I64]
     L.lwm_blockattn_bwd.restype = ctypes.c_int
     L.lwm_blockattn_bwd.argtypes = [P, P, P, P, VP, P, VP, VP, I64, I64, I32, F32, P, P, P, VP, ctypes.c_size_t, VP]
     L.lwm_blockattn_bwd_noalloc.restype = ctypes.c_int
@@ -211,16 +213,53 @@ def lwm_blockattn_bwd_workspace_size(B, H, Lq, Lk, D) -> int:
     return int(lib().lwm_blockattn_bwd_workspace_size(B, H, Lq, Lk, D))
 
 
+def lwm_blockattn_bwd_workspace_size_ds(B, H, Lq, Lk, D, heads_per_pass) -> int:
+    return int(lib().lwm_blockattn_bwd_workspace_size_ds(B, H, Lq, Lk, D, heads_per_pass))
+
+
+# Device memory the binding gives the stored dS when it allocates a backward workspace itself.
+DS_BUDGET_BYTES = 64 << 30
+
+
+# Fewest (batch, head) pairs per pass for which the binding picks the stored-dS backward: with
+# fewer, each pass's launches leave too much of the chip idle at their ends (measured on a packed
+# row of 65536 tokens: 8 pairs per pass slower than recomputing, 16 faster).
+DS_MIN_HEADS = 16
+
+
+def default_ds_heads(B, H, Lq, Lk, D, budget=DS_BUDGET_BYTES) -> int:
+    """(batch, head) pairs per pass of the stored-dS backward whose slots fit in ``budget`` bytes:
+    all B*H if they fit, else the largest multiple of 8; 0 (the recomputing path) when fewer than
+    min(B*H, DS_MIN_HEADS) fit."""
+    slot = lwm_blockattn_bwd_workspace_size_ds(B, H, Lq, Lk, D, 1) - lwm_blockattn_bwd_workspace_size(B, H, Lq, Lk, D)
+    if slot <= 0:
+        return 0
+    bh = B * H
+    g = min(bh, budget // slot)
+    if g < bh:
+        g -= g % 8
+    return g if g >= min(bh, DS_MIN_HEADS) else 0
+
+
+def bwd_workspace(B, H, Lq, Lk, D, device, ds_heads=None):
+    """A backward workspace for these sizes: with room for the stored dS of ``ds_heads`` pairs
+    per pass (None: ``default_ds_heads``; 0: none, the recomputing path)."""
+    heads = default_ds_heads(B, H, Lq, Lk, D) if ds_heads is None else int(ds_heads)
+    size = (lwm_blockattn_bwd_workspace_size_ds(B, H, Lq, Lk, D, heads) if heads > 0
+            else lwm_blockattn_bwd_workspace_size(B, H, Lq, Lk, D))
+    return torch.empty(size, dtype=torch.uint8, device=device)
+
+
 def lwm_blockattn_bwd(q, k, v, o, lse, dout, seg_q=None, seg_k=None, q_offset=0, k_offset=0, causal=True,
-                      scale=0.0, dq=None, dk=None, dv=None, workspace=None):
-    """Backward; returns (dq, dk, dv) w.r.t. the operands given (the rotated Q', K')."""
+                      scale=0.0, dq=None, dk=None, dv=None, workspace=None, ds_heads=None):
+    """Backward; returns (dq, dk, dv) w.r.t. the operands given (the rotated Q', K').  Without a
+    ``workspace`` one is allocated with room for ``ds_heads`` (see ``bwd_workspace``)."""
     B, Lq, H, D = q.shape
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    need = lwm_blockattn_bwd_workspace_size(B, H, Lq, k.shape[1], D)
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = bwd_workspace(B, H, Lq, k.shape[1], D, q.device, ds_heads)
     d, Lk = q.device, k.shape[1]
     _check(lib().lwm_blockattn_bwd(_ref(tensor4(q, "q", d)), _ref(tensor4(k, "k", d)), _ref(tensor4(v, "v", d)),
                                    _ref(tensor4(o, "o", d)), _ptr(_rows(lse, B, H, Lq, d, "lse")),
@@ -277,15 +316,14 @@ def lwm_blockattn_fwd_rope(q, k, v, theta, seg_q=None, seg_k=None, q_offset=0, k
 
 def lwm_blockattn_bwd_rope(q_rot, k_rot, v, o, lse, dout, theta, seg_q=None, seg_k=None, q_offset=0, k_offset=0,
                            causal=True, scale=0.0, layout="half", restart=False, q_pos_offset=0, k_pos_offset=0,
-                           dq=None, dk=None, dv=None, workspace=None):
+                           dq=None, dk=None, dv=None, workspace=None, ds_heads=None):
     """Backward with the inverse RoPE inside the call; returns (dq, dk, dv) w.r.t. the pre-RoPE Q, K."""
     B, Lq, H, D = q_rot.shape
     dq = torch.empty_like(q_rot) if dq is None else dq
     dk = torch.empty_like(k_rot) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     if workspace is None:
-        workspace = torch.empty(lwm_blockattn_bwd_workspace_size(B, H, Lq, k_rot.shape[1], D), dtype=torch.uint8,
-                                device=q_rot.device)
+        workspace = bwd_workspace(B, H, Lq, k_rot.shape[1], D, q_rot.device, ds_heads)
     ra = rope_args(theta, layout, restart, q_pos_offset, k_pos_offset)
     d, Lk = q_rot.device, k_rot.shape[1]
     _check(lib().lwm_blockattn_bwd_rope(_ref(tensor4(q_rot, "q_rot", d)), _ref(tensor4(k_rot, "k_rot", d)),
@@ -319,17 +357,18 @@ RING_BWD_REUSE_WORKSPACE = 1
 
 
 def lwm_ring_step_bwd(q, k_shard, v_shard, o, lse, dout, dq_acc, dk_acc, dv_acc, seg_q=None, seg_k=None,
-                      q_offset=0, k_offset=0, causal=True, scale=0.0, workspace=None, reuse_workspace=False):
+                      q_offset=0, k_offset=0, causal=True, scale=0.0, workspace=None, reuse_workspace=False,
+                      ds_heads=None):
     """Add one KV shard's share of the gradients into dq_acc (float32, like q) and dk_acc,
     dv_acc (float32, like k_shard), in place; o and lse are the forward's results over all shards.
     ``reuse_workspace``: the workspace already holds this query block's delta and rescaled lse
-    from an earlier step of the same ring (same q, o, lse, dout), so that pass is skipped."""
+    from an earlier step of the same ring (same q, o, lse, dout), so that pass is skipped.
+    Without a ``workspace`` one is allocated with room for ``ds_heads`` (see ``bwd_workspace``)."""
     B, Lq, H, D = q.shape
-    need = lwm_blockattn_bwd_workspace_size(B, H, Lq, k_shard.shape[1], D)
     if workspace is None:
         if reuse_workspace:
             raise ValueError("reuse_workspace needs the workspace an earlier step of the ring wrote")
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = bwd_workspace(B, H, Lq, k_shard.shape[1], D, q.device, ds_heads)
     d, Lk = q.device, k_shard.shape[1]
     _check(lib().lwm_ring_step_bwd(_ref(tensor4(q, "q", d)), _ref(tensor4(k_shard, "k_shard", d)),
                                    _ref(tensor4(v_shard, "v_shard", d)), _ref(tensor4(o, "o", d)),

@@ -45,13 +45,16 @@ def ring_forward(q_rot, k_shards, v_shards, shard_order, shard_len, q_offset, ca
 
 
 def ring_backward(q_rot, k_shards, v_shards, o, lse, dout, shard_order, shard_len, q_offset, causal=True,
-                  scale=0.0, seg_q=None, seg_k_shards=None, dq_acc=None, dk_acc=None, dv_acc=None, workspace=None):
+                  scale=0.0, seg_q=None, seg_k_shards=None, dq_acc=None, dk_acc=None, dv_acc=None, workspace=None,
+                  ds_heads=None):
     """Backward ring for one query block: visit the KV shards in ``shard_order`` and add each
     shard's share of the gradients into ``dq_acc`` (float32 [B, Lq, H, D]) and into the shard's
     own ``dk_acc[j]``, ``dv_acc[j]`` (float32 [B, shard_len, H, D]; on a ring these travel with
     the shard).  o and lse are the forward's results over all shards (``ring_forward``).  Shards
     wholly in the causal future of the block are skipped: they add zero.  Accumulators that are
-    not given start at zero.  Returns (dq_acc, dk_acc, dv_acc), the last two dicts by shard.
+    not given start at zero.  Without a ``workspace`` one is allocated with room for the stored
+    dS of ``ds_heads`` pairs per pass (``lwm.bwd_workspace``).  Returns (dq_acc, dk_acc, dv_acc),
+    the last two dicts by shard.
     """
     B, Lq, H, D = q_rot.shape
     dev = q_rot.device
@@ -60,8 +63,7 @@ def ring_backward(q_rot, k_shards, v_shards, o, lse, dout, shard_order, shard_le
     dk_acc = {} if dk_acc is None else dk_acc
     dv_acc = {} if dv_acc is None else dv_acc
     if workspace is None:
-        need = lwm.lwm_blockattn_bwd_workspace_size(B, H, Lq, shard_len, D)
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = lwm.bwd_workspace(B, H, Lq, shard_len, D, dev, ds_heads)
     last_q = q_offset + Lq - 1
     first = True  # the first visited shard writes the block's delta and rescaled lse; the rest reuse them
     for j in shard_order:
@@ -93,9 +95,10 @@ def attention_forward(q, k, v, theta, seg=None, layout="half", causal=True, scal
 
 
 class TrainStepBuffers:
-    """Device buffers of one training step, allocated once and reused across steps."""
+    """Device buffers of one training step, allocated once and reused across steps.  The backward
+    workspace has room for the stored dS of ``ds_heads`` pairs per pass (``lwm.bwd_workspace``)."""
 
-    def __init__(self, q, k):
+    def __init__(self, q, k, ds_heads=None):
         B, L, H, D = q.shape
         Lk = k.shape[1]
         self.qr = torch.empty_like(q)
@@ -105,8 +108,7 @@ class TrainStepBuffers:
         self.dq = torch.empty_like(q)
         self.dk = torch.empty_like(k)
         self.dv = torch.empty_like(k)
-        ws = lwm.lwm_blockattn_bwd_workspace_size(B, H, L, Lk, D)
-        self.workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
+        self.workspace = lwm.bwd_workspace(B, H, L, Lk, D, q.device, ds_heads)
 
 
 def training_step(q, k, v, dout, theta, seg=None, layout="half", causal=True, scale=0.0, buffers=None):

@@ -85,7 +85,7 @@ def run_copy(mib: int):
 
 
 def _short(kernel_name: str) -> str:
-    for key in ("bwd_dkdv", "bwd_dq", "bwd_delta", "attn_fwd_bf16", "attn_fwd_f32", "rope_kernel"):
+    for key in ("bwd_dkdv", "bwd_dq_ds", "bwd_dq", "bwd_delta", "attn_fwd_bf16", "attn_fwd_f32", "rope_kernel"):
         if key in kernel_name:
             return key
     if "ffn_gemm_kernel" in kernel_name:
@@ -164,8 +164,7 @@ def medians(n: int = 20, warm: int = 3) -> dict:
         res[name + " lwm_blockattn_fwd"] = r
         print(f"[medians] {name} forward {r['ms']:.3f} ms", flush=True)
         if w.backward:
-            ws = torch.empty(lwm.lwm_blockattn_bwd_workspace_size(w.B, w.H, w.Lq, w.Lk, w.D), dtype=torch.uint8,
-                             device="cuda")
+            ws = lwm.bwd_workspace(w.B, w.H, w.Lq, w.Lk, w.D, "cuda")
             dq, dk, dv = torch.empty_like(qr), torch.empty_like(kr), torch.empty_like(d["v"])
             r = timed(lambda: lwm.lwm_blockattn_bwd(qr, kr, d["v"], o, lse, d["do"], seg, seg, dq=dq, dk=dk, dv=dv,
                                                     workspace=ws))

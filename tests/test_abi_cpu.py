@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol():
     assert set(names) == set(lwm.EXPORTS), names
     for n in names:
         assert hasattr(L, n), n
-    assert L.lwm_abi_version() == 6
+    assert L.lwm_abi_version() == 7
     assert L.lwm_last_error() == b""
 
 
@@ -293,3 +293,36 @@ def test_mfma_probe_binding_rejects_host_and_misshapen_tensors():
     import torch
     with pytest.raises(ValueError, match="GPU tensor"):
         lwm.lwm_probe_mfma_bf16(torch.zeros(256 * 128, dtype=torch.bfloat16), 8)
+
+
+def test_stored_ds_workspace_size():
+    """lwm_blockattn_bwd_workspace_size_ds: the two float32 rows per query, then one slot of
+    Lk rounded up to 64 rows of Lq rounded up to 256 bf16 values per (batch, head) pair of a pass."""
+    L = _lib()
+    base = L.lwm_blockattn_bwd_workspace_size(2, 3, 300, 500, 128)
+    slot = 512 * 512 * 2
+    assert L.lwm_blockattn_bwd_workspace_size_ds(2, 3, 300, 500, 128, 4) == base + 4 * slot
+    assert L.lwm_blockattn_bwd_workspace_size_ds(2, 3, 300, 500, 128, 100) == base + 6 * slot  # clamped to B*H
+    assert L.lwm_blockattn_bwd_workspace_size_ds(1, 1, 256, 7, 128, 1) == L.lwm_blockattn_bwd_workspace_size(
+        1, 1, 256, 7, 128) + 64 * 256 * 2
+    for args in ((2, 3, 300, 500, 128, 0), (2, 3, 300, 500, 128, -5), (2, 3, 300, 0, 128, 4),
+                 (1, 1, (1 << 21) + 1, 64, 128, 1)):
+        assert L.lwm_blockattn_bwd_workspace_size_ds(*args) == L.lwm_blockattn_bwd_workspace_size(*args[:5]), args
+    assert L.lwm_blockattn_bwd_workspace_size_ds(0, 3, 300, 500, 128, 4) == 256
+    assert L.lwm_blockattn_bwd_workspace_size_ds(64, 64, 1 << 21, 1 << 31, 128, 4096) == 2**64 - 1
+
+
+def test_default_stored_ds_heads():
+    """The binding's choice of pairs per pass for the workspaces it allocates (64 GiB of dS)."""
+    assert lwm.DS_BUDGET_BYTES == 64 << 30
+    assert lwm.default_ds_heads(1, 32, 32768, 32768, 128) == 32  # 32 slots of 2 GiB
+    assert lwm.default_ds_heads(1, 32, 65536, 65536, 128) == 0  # 8 GiB slots: 8 per pass, under 16
+    assert lwm.default_ds_heads(1, 32, 65536, 65536, 128, budget=130 << 30) == 16  # a multiple of 8
+    assert lwm.default_ds_heads(1, 4, 1 << 20, 1 << 20, 128) == 0  # not one slot fits
+    slot = 4096 * 4096 * 2
+    assert lwm.default_ds_heads(1, 12, 4096, 4096, 128, budget=12 * slot) == 12
+    assert lwm.default_ds_heads(1, 12, 4096, 4096, 128, budget=11 * slot) == 0
+    assert lwm.default_ds_heads(1, 40, 4096, 4096, 128, budget=39 * slot) == 32
+    assert lwm.default_ds_heads(1, 4, 4096, 4096, 128, budget=4 * slot) == 4
+    assert lwm.default_ds_heads(1, 4, 4096, 4096, 128, budget=3 * slot) == 0
+    assert lwm.default_ds_heads(2, 8, 4096, 4096, 128, budget=16 * slot) == 16
