@@ -303,6 +303,7 @@ constexpr int kDsQueries = kDsWaves * 32;  // queries per workgroup
 constexpr int kDsBlock = 64;
 constexpr int kDsBlockBytes = kDsBlock * kDsBlock * 2;
 constexpr int kDsChunkBytes = kDsBlock * 16;  // one chunk of all 64 keys of a block
+constexpr int kCachePolicyNT = 2;  // buffer instruction cache policy: non-temporal (gfx950 nt bit)
 __device__ __forceinline__ int64_t ds_slot_bytes(const BwdParams& p) {
   return (int64_t)((p.Lk + kDsBlock - 1) / kDsBlock) * (p.ds_ld / kDsBlock) * kDsBlockBytes;
 }
@@ -783,7 +784,9 @@ __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams 
       const bf16x8 dsb[2] = {pack8(dp, 0), pack8(dp, 1)};
       if constexpr (kStoreDs) {
         // dsb[u] holds queries q0 + 16u + 8*h32 + 0..7: chunk (q0 % 64) / 8 + 2u + h32 of this
-        // lane's key in the stored layout
+        // lane's key in the stored layout.  The stores are marked non-temporal (cache policy
+        // bit nt): nothing reads dS again before the dQ kernel, and measured, that kernel then
+        // runs 3-4% faster (the dK/dV kernel is unchanged).
         // the lane's part (row c32, chunk + h32) comes from threadIdx.x itself: a value kept for the
         // loop is spilled, and its reload would wait for the next tile's loads
         const int tx = (int)threadIdx.x;
@@ -792,7 +795,7 @@ __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams 
 #pragma unroll
         for (int u = 0; u < 2; ++u)
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, dsb[u]), rds, off + 2 * u * kDsChunkBytes,
-                                                 0, 0);
+                                                 0, kCachePolicyNT);
       }
       // dV^T += dO^T P, dK^T += Q^T dS (transposed operands by transposing reads, one step ahead)
       {
