@@ -261,7 +261,7 @@ def bench_extras(torch, lwm, path, workloads, configs, steps=3, warmup=1):
     dq_acc = torch.empty((w.B, S, w.H, w.D), **f32)
     dk_acc = {j: torch.empty((w.B, S, w.H, w.D), **f32) for j in kr}
     dv_acc = {j: torch.empty((w.B, S, w.H, w.D), **f32) for j in kr}
-    ws = lwm.bwd_workspace(w.B, w.H, S, S, w.D, "cuda")
+    ws = lwm.bwd_workspace(w.B, w.H, S, S, w.D, "cuda", causal=False)  # dense: every shard offset
 
     def ring_bwd_step():
         for t in (dq_acc, *dk_acc.values(), *dv_acc.values()):

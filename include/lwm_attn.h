@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define LWM_ABI_VERSION 7
+#define LWM_ABI_VERSION 8
 
 typedef enum {
   LWM_OK = 0,
@@ -127,14 +127,19 @@ size_t lwm_blockattn_bwd_workspace_size(int64_t B, int64_t H, int64_t Lq, int64_
 
 /*
  * Bytes of workspace with room for the stored-dS backward over heads_per_pass (batch, head)
- * pairs at a time: lwm_blockattn_bwd_workspace_size() plus heads_per_pass slots of
- * Lk64 * ldq * 2 bytes, Lk64 = Lk rounded up to 64 and ldq = Lq rounded up to 256 (each slot
- * holds one pair's dS^T in bf16).  heads_per_pass
- * is clamped to B * H; the minimum size comes back for heads_per_pass <= 0, empty sizes, or Lq
- * above 2^21 (no stored-dS path), SIZE_MAX if the size does not fit in a size_t.  How a larger
- * workspace is used is described at lwm_blockattn_bwd.
+ * pairs at a time, for a call with these sizes, offsets and causal flag:
+ * lwm_blockattn_bwd_workspace_size() plus heads_per_pass slots.  A slot holds one pair's dS^T
+ * (bf16) in 64 x 64 blocks: Lk rounded up to 64 key rows by ldq = Lq rounded up to 256 queries,
+ * less, under the causal mask, the blocks of query blocks before a key block's first visible
+ * query (q_offset + q >= k_offset + k): key block kb keeps query blocks from
+ * clamp(kb + floor((k_offset - q_offset) / 64), 0, ldq / 64) on (about half of a square slot).
+ * heads_per_pass is clamped to B * H; the minimum size comes back for heads_per_pass <= 0, empty
+ * sizes, offsets outside [0, 2^40], Lq above 2^21 or nothing to store (no stored-dS path),
+ * SIZE_MAX if the size does not fit in a size_t.  How a larger workspace is used is described at
+ * lwm_blockattn_bwd.
  */
 size_t lwm_blockattn_bwd_workspace_size_ds(int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
+                                           int64_t q_offset, int64_t k_offset, int32_t causal,
                                            int64_t heads_per_pass);
 
 /*

@@ -3,6 +3,7 @@
 // leaves a message for lwm_last_error() on the calling thread.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -245,24 +246,45 @@ size_t lwm_blockattn_bwd_workspace_size(int64_t B, int64_t H, int64_t Lq, int64_
 
 namespace {
 
-// Stored dS: one (batch, head) pair's dS^T is Lk rounded up to 64 rows of Lq rounded up to 256
-// bf16 values (in blocks of 64 x 64).  The kernels address a workgroup's rows with 32-bit
-// offsets, so rows are at most kMaxDsLd values.
+// Stored dS: one (batch, head) pair's dS^T in 64 x 64 blocks (8 KB), rows of Lq rounded up to 256
+// values.  Under the causal mask key block kb is seen by no query block before
+// qlo(kb) = clamp(kb + shift, 0, nqb), shift = floor((k_offset - q_offset) / 64), and its row starts
+// there (the kernels use the same closed forms).  The kernels address a workgroup's rows with
+// 32-bit offsets, so rows are at most kMaxDsLd values.
 constexpr int64_t kMaxDsLd = int64_t(1) << 21;
+constexpr int64_t kDsNoShift = -(int64_t(1) << 40);  // without the causal mask: every block stored
 int64_t ds_row_len(int64_t Lq) { return (Lq + 255) / 256 * 256; }
-size_t ds_slot_bytes(int64_t Lq, int64_t Lk) { return (size_t)((Lk + 63) / 64 * 64) * (size_t)ds_row_len(Lq) * 2; }
+int64_t ds_shift(int64_t q_offset, int64_t k_offset, int32_t causal) {
+  if (!causal) return kDsNoShift;
+  const int64_t d = k_offset - q_offset;
+  return d >= 0 ? d / 64 : -((-d + 63) / 64);  // floor(d / 64)
+}
+// Blocks stored for key blocks 0 .. kb - 1 (rows of nqb blocks less the causally invisible ones).
+int64_t ds_row_start(int64_t kb, int64_t nqb, int64_t c) {
+  const int64_t a = std::max<int64_t>(0, -c), e = std::max(a, nqb - c);
+  const int64_t m = std::min(std::max(kb, a), e);
+  const int64_t lo_sum = (m - a) * c + (a + m - 1) * (m - a) / 2;
+  return kb * nqb - (lo_sum + nqb * std::max<int64_t>(0, kb - e));
+}
+int64_t ds_slot_blocks(int64_t Lq, int64_t Lk, int64_t shift) {
+  return ds_row_start((Lk + 63) / 64, ds_row_len(Lq) / 64, shift);
+}
 
 }  // namespace
 
 extern "C" {
 
 size_t lwm_blockattn_bwd_workspace_size_ds(int64_t B, int64_t H, int64_t Lq, int64_t Lk, int64_t D,
+                                           int64_t q_offset, int64_t k_offset, int32_t causal,
                                            int64_t heads_per_pass) {
   const size_t base = lwm_blockattn_bwd_workspace_size(B, H, Lq, Lk, D);
   if (B <= 0 || H <= 0 || Lq <= 0 || Lk <= 0 || heads_per_pass <= 0) return base;
   const int64_t ld = ds_row_len(Lq);
-  if (ld > kMaxDsLd || Lk > (int64_t(1) << 31)) return base;
-  const size_t slot = ds_slot_bytes(Lq, Lk);
+  const int64_t kOff = int64_t(1) << 40;  // the offsets the calls accept
+  if (ld > kMaxDsLd || Lk > (int64_t(1) << 31) || q_offset < 0 || k_offset < 0 || q_offset > kOff || k_offset > kOff)
+    return base;
+  const size_t slot = (size_t)ds_slot_blocks(Lq, Lk, ds_shift(q_offset, k_offset, causal)) * 8192;
+  if (slot == 0) return base;
   const size_t heads = (size_t)(heads_per_pass < B * H ? heads_per_pass : B * H);
   if (heads > (SIZE_MAX - base) / slot) return SIZE_MAX;
   return base + heads * slot;
@@ -305,8 +327,9 @@ int prepare_bwd(const lwm_tensor4* q, const lwm_tensor4* k, const lwm_tensor4* v
   // dK/dV kernel writes dS and dQ is formed from it.  Passes take whole multiples of 8 pairs (one
   // per XCD) unless every pair fits in one.
   if (!empty && workspace && q->L > 0 && k->L > 0 && ds_row_len(q->L) <= kMaxDsLd) {
-    const int64_t ld = ds_row_len(q->L), BH = q->B * q->H;
-    const size_t slot = ds_slot_bytes(q->L, k->L);
+    const int64_t ld = ds_row_len(q->L), BH = q->B * q->H, shift = ds_shift(q_offset, k_offset, causal);
+    const int64_t blocks = ds_slot_blocks(q->L, k->L, shift);
+    const size_t slot = (size_t)std::max<int64_t>(blocks, 1) * 8192;
     const size_t room = (workspace_bytes - need) / slot;
     int64_t g = room < (size_t)BH ? (int64_t)room : BH;
     if (g < BH && g >= 8) g &= ~int64_t(7);
@@ -314,6 +337,8 @@ int prepare_bwd(const lwm_tensor4* q, const lwm_tensor4* k, const lwm_tensor4* v
       p->ds = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + need);
       p->ds_ld = ld;
       p->ds_heads = (int)g;
+      p->ds_shift = shift;
+      p->ds_slot_blocks = blocks;
     }
   }
   p->B = (int)q->B; p->H = (int)q->H; p->Lq = (int)q->L; p->Lk = (int)k->L;

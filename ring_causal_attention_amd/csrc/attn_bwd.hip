@@ -304,8 +304,20 @@ constexpr int kDsBlock = 64;
 constexpr int kDsBlockBytes = kDsBlock * kDsBlock * 2;
 constexpr int kDsChunkBytes = kDsBlock * 16;  // one chunk of all 64 keys of a block
 constexpr int kCachePolicyNT = 2;  // buffer instruction cache policy: non-temporal (gfx950 nt bit)
-__device__ __forceinline__ int64_t ds_slot_bytes(const BwdParams& p) {
-  return (int64_t)((p.Lk + kDsBlock - 1) / kDsBlock) * (p.ds_ld / kDsBlock) * kDsBlockBytes;
+__device__ __forceinline__ int64_t ds_slot_bytes(const BwdParams& p) { return p.ds_slot_blocks * kDsBlockBytes; }
+// Under the causal mask key block kb is seen by no query block before qlo(kb), so its row of
+// blocks starts there; the rows follow each other without gaps.  Both in closed form (the same
+// arithmetic as the host's workspace sizing).
+__device__ __forceinline__ int64_t ds_qlo(const BwdParams& p, int64_t kb) {
+  return imin64(imax64(kb + p.ds_shift, 0), p.ds_ld / kDsBlock);
+}
+// Blocks stored for key blocks 0 .. kb - 1.
+__device__ __forceinline__ int64_t ds_row_start(const BwdParams& p, int64_t kb) {
+  const int64_t nqb = p.ds_ld / kDsBlock, c = p.ds_shift;
+  const int64_t a = imax64(0, -c), e = imax64(a, nqb - c);  // qlo = 0 below a, nqb from e on
+  const int64_t m = imin64(imax64(kb, a), e);                // qlo = i + c for a <= i < m
+  const int64_t lo_sum = (m - a) * c + (a + m - 1) * (m - a) / 2;
+  return kb * nqb - (lo_sum + nqb * imax64(0, kb - e));
 }
 struct StageDs {
   uint8_t k[kTileBytes];                 // K rows, row-major swizzled
@@ -369,17 +381,16 @@ __global__ __launch_bounds__(kDsWaves * kWave) void bwd_dq_ds_kernel(BwdParams p
   const uint8_t* kg = reinterpret_cast<const uint8_t*>(p.k + b * p.sk.b + hh * p.sk.h);
   const int64_t kl_bytes = p.sk.l * 2;
   const int64_t k_extent = (int64_t)(p.Lk - 1) * kl_bytes + 256;
-  // this pair's dS^T blocks (see ds_block_row): the tile of keys k0.. is the four blocks of
-  // query blocks q0/64 .. + 3 of key block k0/64, 32 KB in a row
-  const uint8_t* sg = reinterpret_cast<const uint8_t*>(p.ds) + (int64_t)lbh * ds_slot_bytes(p) +
-                      (int64_t)(q0 / kDsBlock) * kDsBlockBytes;
-  const int64_t ds_row_bytes = p.ds_ld / kDsBlock * kDsBlockBytes;  // one key block's row of blocks
+  // this pair's dS^T blocks: the tile of keys k0.. is query blocks q0/64 .. + 3 of key block
+  // k0/64, 32 KB in a row, of which those before the row's first stored block are not read
+  const uint8_t* sg = reinterpret_cast<const uint8_t*>(p.ds) + (int64_t)lbh * ds_slot_bytes(p);
+  const int64_t nqb = p.ds_ld / kDsBlock;
   const int32_t* segk_row = segs ? p.seg_k + (int64_t)b * p.Lk : nullptr;
   // K tile: 16 blocks of 1 KB, two per wave; dS^T tile: 32 blocks of 1 KB, four per wave.  In
   // LDS the dS^T tile is two row-major swizzled 64 x 128 tiles side by side (queries 0..127 and
   // 128..255 of the workgroup): 16-byte chunk c of row r of half hr is chunk c % 8 of key r in
   // query block 2 hr + c / 8
-  int ld_voff_k[2], ld_voff_s[4];
+  int ld_voff_k[2], ld_voff_s[4], ld_blk_s[4];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     const int row = (w * 2 + r) * 4 + (lane >> 4);
@@ -389,16 +400,25 @@ __global__ __launch_bounds__(kDsWaves * kWave) void bwd_dq_ds_kernel(BwdParams p
   for (int r = 0; r < 4; ++r) {
     const int blk = w * 4 + r, hr = blk >> 4, row = (blk & 15) * 4 + (lane >> 4);
     const int c = (lane & 15) ^ swz16(row);
-    ld_voff_s[r] = (2 * hr + (c >> 3)) * kDsBlockBytes + (c & 7) * kDsChunkBytes + row * 16;
+    ld_blk_s[r] = 2 * hr + (c >> 3);
+    ld_voff_s[r] = (c & 7) * kDsChunkBytes + row * 16;
   }
   auto issue = [&](int tile, StageDs& dst) __attribute__((always_inline)) {
     const int k0 = tile * BN;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + k0 * kl_bytes, k_extent - k0 * kl_bytes);
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(sg + (int64_t)(k0 / kDsBlock) * ds_row_bytes, 4 * kDsBlockBytes);
+    const int64_t kb = k0 / kDsBlock, qlo = ds_qlo(p, kb);
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(sg + ds_row_start(p, kb) * kDsBlockBytes, (nqb - qlo) * kDsBlockBytes);
+    const int rel0 = (int)(q0 / kDsBlock - qlo);  // this tile's first query block in the row
+    // a block before the row's first (none of its pairs is visible) gets an offset past the end
+    int voff_s[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      voff_s[r] = rel0 + ld_blk_s[r] >= 0 ? (rel0 + ld_blk_s[r]) * kDsBlockBytes + ld_voff_s[r] : 0x7fffffff;
 #pragma unroll
     for (int r = 0; r < 2; ++r) load_lds16(rk, &dst.k[(w * 2 + r) * 1024], ld_voff_k[r]);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) load_lds16(rs, &dst.s[(w * 4 + r) * 1024], ld_voff_s[r]);
+    for (int r = 0; r < 4; ++r) load_lds16(rs, &dst.s[(w * 4 + r) * 1024], voff_s[r]);
     if (segs && w == 0) load_lds4(make_rsrc(segk_row + k0, (int64_t)(p.Lk - k0) * 4), &dst.seg[0], lane * 4);
   };
   int tlo0, thi0;
@@ -566,13 +586,15 @@ __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams 
   // last key block fall outside the resource and their stores are dropped).  Lane (c32, h32)
   // writes key w*32 + c32 of them, chunks 2u + h32 of a sub-tile.
   __amdgpu_buffer_rsrc_t rds;
-  int ds_wave = 0;  // the wave's part of the store offsets (its keys' block and rows); wave-uniform
+  int ds_wave = 0;   // the wave's part of the store offsets (its key block's row and keys); uniform
+  int ds_qlo_w = 0;  // the first query block stored in the wave's key block's row
   if constexpr (kStoreDs) {
-    const int64_t row_bytes = p.ds_ld / kDsBlock * kDsBlockBytes;
-    const int kb0 = k0 / kDsBlock, nkb = (p.Lk + kDsBlock - 1) / kDsBlock;
-    rds = make_rsrc(reinterpret_cast<const uint8_t*>(p.ds) + (int64_t)lbh * ds_slot_bytes(p) + kb0 * row_bytes,
-                    (int64_t)(nkb - kb0) * row_bytes);
-    ds_wave = (w >> 1) * (int)row_bytes + (w & 1) * 32 * 16;
+    const int64_t kb0 = k0 / kDsBlock, nkb = (p.Lk + kDsBlock - 1) / kDsBlock;
+    const int64_t row0 = ds_row_start(p, kb0), kbw = kb0 + (w >> 1);
+    rds = make_rsrc(reinterpret_cast<const uint8_t*>(p.ds) + (int64_t)lbh * ds_slot_bytes(p) + row0 * kDsBlockBytes,
+                    (ds_row_start(p, imin64(kb0 + 4, nkb)) - row0) * kDsBlockBytes);
+    ds_qlo_w = (int)ds_qlo(p, kbw);
+    ds_wave = (int)((ds_row_start(p, kbw) - row0 - ds_qlo_w) * kDsBlockBytes) + (w & 1) * 32 * 16;
   }
 
   // this wave's 32 V rows into its 8 KB of LDS (8 blocks of 1 KB; rows past the end read as zero),
@@ -782,7 +804,9 @@ __global__ __launch_bounds__(kDkdvWaves * kWave) void bwd_dkdv_kernel(BwdParams 
       }
       const bf16x8 pb[2] = {pack8(s, 0), pack8(s, 1)};
       const bf16x8 dsb[2] = {pack8(dp, 0), pack8(dp, 1)};
-      if constexpr (kStoreDs) {
+      // a visible pair's query block is never before its key block's first stored one (the causal
+      // test above bounds it); the check keeps a conservative segment test from writing elsewhere
+      if (kStoreDs && q0 / kDsBlock >= ds_qlo_w) {
         // dsb[u] holds queries q0 + 16u + 8*h32 + 0..7: chunk (q0 % 64) / 8 + 2u + h32 of this
         // lane's key in the stored layout.  The stores are marked non-temporal (cache policy
         // bit nt): nothing reads dS again before the dQ kernel, and measured, that kernel then

@@ -99,12 +99,17 @@ struct BwdParams {
   // gradients w.r.t. the pre-RoPE Q and K (stored outputs only, not the ring accumulators)
   RopeFuse rope;
   // Stored dS (ds != nullptr): the (batch, head) pairs go through in passes of ds_heads; in each
-  // pass the dK/dV kernel also writes dS^T (bf16) of pair bh0 + j into slot j (Lk rounded up to
-  // 64 rows of ds_ld = Lq rounded up to 256 values, in 64 x 64 blocks), and a dQ kernel then
+  // pass the dK/dV kernel also writes dS^T (bf16) of pair bh0 + j into slot j (64 x 64 blocks: up
+  // to Lk rounded up to 64 rows of ds_ld = Lq rounded up to 256 values), and a dQ kernel then
   // forms dQ from it and K alone instead of recomputing S and dP.
   uint16_t* ds;
   int64_t ds_ld;
   int ds_heads;
+  // causal compaction of the slots: key block kb stores query blocks from
+  // qlo(kb) = clamp(kb + ds_shift, 0, ds_ld / 64) on (ds_shift = floor((k_offset - q_offset) / 64),
+  // or -2^40 without the causal mask, which stores every block); ds_slot_blocks blocks per slot
+  int64_t ds_shift;
+  int64_t ds_slot_blocks;
   // the (batch, head) pairs one launch covers: bh0 .. bh0 + bh_count - 1 (set by launch_attn_bwd)
   int bh0, bh_count;
 };

@@ -67,7 +67,7 @@ def lib() -> ctypes.CDLL:
     L.lwm_blockattn_bwd_workspace_size.restype = ctypes.c_size_t
     L.lwm_blockattn_bwd_workspace_size.argtypes = [I64, I64, I64, I64, I64]
     L.lwm_blockattn_bwd_workspace_size_ds.restype = ctypes.c_size_t
-    L.lwm_blockattn_bwd_workspace_size_ds.argtypes = [I64, I64, I64, I64, I64, I64]
+    L.lwm_blockattn_bwd_workspace_size_ds.argtypes = [I64, I64, I64, I64, I64, I64, I64, I32, I64]
     L.lwm_blockattn_bwd.restype = ctypes.c_int
     L.lwm_blockattn_bwd.argtypes = [P, P, P, P, VP, P, VP, VP, I64, I64, I32, F32, P, P, P, VP, ctypes.c_size_t, VP]
     L.lwm_blockattn_bwd_noalloc.restype = ctypes.c_int
@@ -213,12 +213,14 @@ def lwm_blockattn_bwd_workspace_size(B, H, Lq, Lk, D) -> int:
     return int(lib().lwm_blockattn_bwd_workspace_size(B, H, Lq, Lk, D))
 
 
-def lwm_blockattn_bwd_workspace_size_ds(B, H, Lq, Lk, D, heads_per_pass) -> int:
-    return int(lib().lwm_blockattn_bwd_workspace_size_ds(B, H, Lq, Lk, D, heads_per_pass))
+def lwm_blockattn_bwd_workspace_size_ds(B, H, Lq, Lk, D, heads_per_pass, q_offset=0, k_offset=0, causal=True) -> int:
+    return int(lib().lwm_blockattn_bwd_workspace_size_ds(B, H, Lq, Lk, D, int(q_offset), int(k_offset),
+                                                         int(bool(causal)), heads_per_pass))
 
 
-# Device memory the binding gives the stored dS when it allocates a backward workspace itself.
-DS_BUDGET_BYTES = 64 << 30
+# Most device memory the binding gives the stored dS when it allocates a backward workspace itself
+# (it allocates only the slots of the pairs per pass it picks).
+DS_BUDGET_BYTES = 80 << 30
 
 
 # Fewest (batch, head) pairs per pass for which the binding picks the stored-dS backward: with
@@ -227,11 +229,12 @@ DS_BUDGET_BYTES = 64 << 30
 DS_MIN_HEADS = 16
 
 
-def default_ds_heads(B, H, Lq, Lk, D, budget=DS_BUDGET_BYTES) -> int:
+def default_ds_heads(B, H, Lq, Lk, D, budget=DS_BUDGET_BYTES, q_offset=0, k_offset=0, causal=True) -> int:
     """(batch, head) pairs per pass of the stored-dS backward whose slots fit in ``budget`` bytes:
     all B*H if they fit, else the largest multiple of 8; 0 (the recomputing path) when fewer than
     min(B*H, DS_MIN_HEADS) fit."""
-    slot = lwm_blockattn_bwd_workspace_size_ds(B, H, Lq, Lk, D, 1) - lwm_blockattn_bwd_workspace_size(B, H, Lq, Lk, D)
+    slot = (lwm_blockattn_bwd_workspace_size_ds(B, H, Lq, Lk, D, 1, q_offset, k_offset, causal)
+            - lwm_blockattn_bwd_workspace_size(B, H, Lq, Lk, D))
     if slot <= 0:
         return 0
     bh = B * H
@@ -241,11 +244,13 @@ def default_ds_heads(B, H, Lq, Lk, D, budget=DS_BUDGET_BYTES) -> int:
     return g if g >= min(bh, DS_MIN_HEADS) else 0
 
 
-def bwd_workspace(B, H, Lq, Lk, D, device, ds_heads=None):
-    """A backward workspace for these sizes: with room for the stored dS of ``ds_heads`` pairs
-    per pass (None: ``default_ds_heads``; 0: none, the recomputing path)."""
-    heads = default_ds_heads(B, H, Lq, Lk, D) if ds_heads is None else int(ds_heads)
-    size = (lwm_blockattn_bwd_workspace_size_ds(B, H, Lq, Lk, D, heads) if heads > 0
+def bwd_workspace(B, H, Lq, Lk, D, device, ds_heads=None, q_offset=0, k_offset=0, causal=True):
+    """A backward workspace for a call with these sizes, offsets and causal flag: with room for
+    the stored dS of ``ds_heads`` pairs per pass (None: ``default_ds_heads``; 0: none, the
+    recomputing path).  Sized with causal=False it suits any offsets."""
+    heads = (default_ds_heads(B, H, Lq, Lk, D, q_offset=q_offset, k_offset=k_offset, causal=causal)
+             if ds_heads is None else int(ds_heads))
+    size = (lwm_blockattn_bwd_workspace_size_ds(B, H, Lq, Lk, D, heads, q_offset, k_offset, causal) if heads > 0
             else lwm_blockattn_bwd_workspace_size(B, H, Lq, Lk, D))
     return torch.empty(size, dtype=torch.uint8, device=device)
 
@@ -259,7 +264,7 @@ def lwm_blockattn_bwd(q, k, v, o, lse, dout, seg_q=None, seg_k=None, q_offset=0,
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     if workspace is None:
-        workspace = bwd_workspace(B, H, Lq, k.shape[1], D, q.device, ds_heads)
+        workspace = bwd_workspace(B, H, Lq, k.shape[1], D, q.device, ds_heads, q_offset, k_offset, causal)
     d, Lk = q.device, k.shape[1]
     _check(lib().lwm_blockattn_bwd(_ref(tensor4(q, "q", d)), _ref(tensor4(k, "k", d)), _ref(tensor4(v, "v", d)),
                                    _ref(tensor4(o, "o", d)), _ptr(_rows(lse, B, H, Lq, d, "lse")),
@@ -323,7 +328,7 @@ def lwm_blockattn_bwd_rope(q_rot, k_rot, v, o, lse, dout, theta, seg_q=None, seg
     dk = torch.empty_like(k_rot) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     if workspace is None:
-        workspace = bwd_workspace(B, H, Lq, k_rot.shape[1], D, q_rot.device, ds_heads)
+        workspace = bwd_workspace(B, H, Lq, k_rot.shape[1], D, q_rot.device, ds_heads, q_offset, k_offset, causal)
     ra = rope_args(theta, layout, restart, q_pos_offset, k_pos_offset)
     d, Lk = q_rot.device, k_rot.shape[1]
     _check(lib().lwm_blockattn_bwd_rope(_ref(tensor4(q_rot, "q_rot", d)), _ref(tensor4(k_rot, "k_rot", d)),
@@ -368,7 +373,7 @@ def lwm_ring_step_bwd(q, k_shard, v_shard, o, lse, dout, dq_acc, dk_acc, dv_acc,
     if workspace is None:
         if reuse_workspace:
             raise ValueError("reuse_workspace needs the workspace an earlier step of the ring wrote")
-        workspace = bwd_workspace(B, H, Lq, k_shard.shape[1], D, q.device, ds_heads)
+        workspace = bwd_workspace(B, H, Lq, k_shard.shape[1], D, q.device, ds_heads, q_offset, k_offset, causal)
     d, Lk = q.device, k_shard.shape[1]
     _check(lib().lwm_ring_step_bwd(_ref(tensor4(q, "q", d)), _ref(tensor4(k_shard, "k_shard", d)),
                                    _ref(tensor4(v_shard, "v_shard", d)), _ref(tensor4(o, "o", d)),

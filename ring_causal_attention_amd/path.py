@@ -62,8 +62,8 @@ def ring_backward(q_rot, k_shards, v_shards, o, lse, dout, shard_order, shard_le
         dq_acc = torch.zeros((B, Lq, H, D), dtype=torch.float32, device=dev)
     dk_acc = {} if dk_acc is None else dk_acc
     dv_acc = {} if dv_acc is None else dv_acc
-    if workspace is None:
-        workspace = lwm.bwd_workspace(B, H, Lq, shard_len, D, dev, ds_heads)
+    if workspace is None:  # dense slots (causal=False): the steps differ in k_offset
+        workspace = lwm.bwd_workspace(B, H, Lq, shard_len, D, dev, ds_heads, causal=False)
     last_q = q_offset + Lq - 1
     first = True  # the first visited shard writes the block's delta and rescaled lse; the rest reuse them
     for j in shard_order:
@@ -98,7 +98,7 @@ class TrainStepBuffers:
     """Device buffers of one training step, allocated once and reused across steps.  The backward
     workspace has room for the stored dS of ``ds_heads`` pairs per pass (``lwm.bwd_workspace``)."""
 
-    def __init__(self, q, k, ds_heads=None):
+    def __init__(self, q, k, ds_heads=None, causal=True):
         B, L, H, D = q.shape
         Lk = k.shape[1]
         self.qr = torch.empty_like(q)
@@ -108,7 +108,7 @@ class TrainStepBuffers:
         self.dq = torch.empty_like(q)
         self.dk = torch.empty_like(k)
         self.dv = torch.empty_like(k)
-        self.workspace = lwm.bwd_workspace(B, H, L, Lk, D, q.device, ds_heads)
+        self.workspace = lwm.bwd_workspace(B, H, L, Lk, D, q.device, ds_heads, causal=causal)
 
 
 def training_step(q, k, v, dout, theta, seg=None, layout="half", causal=True, scale=0.0, buffers=None):
@@ -117,7 +117,7 @@ def training_step(q, k, v, dout, theta, seg=None, layout="half", causal=True, sc
     dq and dk are gradients w.r.t. the pre-RoPE q and k: the backward's dQ', dK' are rotated
     back in place by the inverse RoPE.
     """
-    bufs = buffers if buffers is not None else TrainStepBuffers(q, k)
+    bufs = buffers if buffers is not None else TrainStepBuffers(q, k, causal=causal)
     lwm.lwm_rope_apply(q, bufs.qr, seg=seg, theta=theta, layout=layout)
     lwm.lwm_rope_apply(k, bufs.kr, seg=seg, theta=theta, layout=layout)
     lwm.lwm_blockattn_fwd(bufs.qr, bufs.kr, v, seg_q=seg, seg_k=seg, causal=causal, scale=scale, o=bufs.o, lse=bufs.lse)
@@ -134,7 +134,7 @@ def training_step_fused(q, k, v, dout, theta, seg=None, layout="half", causal=Tr
     Positions restart per segment when ``seg`` is given.  Two calls (forward, backward) and five
     kernels instead of seven: no separate RoPE pass over Q and no inverse-RoPE passes over dQ and dK.
     """
-    bufs = buffers if buffers is not None else TrainStepBuffers(q, k)
+    bufs = buffers if buffers is not None else TrainStepBuffers(q, k, causal=causal)
     restart = seg is not None
     lwm.lwm_blockattn_fwd_rope(q, k, v, theta, seg_q=seg, seg_k=seg, causal=causal, scale=scale, layout=layout,
                                restart=restart, o=bufs.o, lse=bufs.lse, q_rot=bufs.qr, k_rot=bufs.kr)

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol():
     assert set(names) == set(lwm.EXPORTS), names
     for n in names:
         assert hasattr(L, n), n
-    assert L.lwm_abi_version() == 7
+    assert L.lwm_abi_version() == 8
     assert L.lwm_last_error() == b""
 
 
@@ -295,31 +295,60 @@ def test_mfma_probe_binding_rejects_host_and_misshapen_tensors():
         lwm.lwm_probe_mfma_bf16(torch.zeros(256 * 128, dtype=torch.bfloat16), 8)
 
 
+def ds_blocks_brute(Lq, Lk, q_offset, k_offset, causal):
+    """Blocks of one stored-dS slot, summed key block by key block: each keeps the 64-query blocks
+    from its first causally visible query block on (all of them without the causal mask)."""
+    nqb, nkb = -(-Lq // 256) * 256 // 64, -(-Lk // 64)
+    total = 0
+    for kb in range(nkb):
+        lo = min(max(kb + (k_offset - q_offset) // 64, 0), nqb) if causal else 0
+        # lo is the block of the first query q with q_offset + q >= k_offset + 64 kb
+        first = max(0, k_offset + 64 * kb - q_offset) if causal else 0
+        assert lo == min(first // 64, nqb)
+        total += nqb - lo
+    return total
+
+
 def test_stored_ds_workspace_size():
-    """lwm_blockattn_bwd_workspace_size_ds: the two float32 rows per query, then one slot of
-    Lk rounded up to 64 rows of Lq rounded up to 256 bf16 values per (batch, head) pair of a pass."""
+    """lwm_blockattn_bwd_workspace_size_ds: the two float32 rows per query, then one slot of 64 x 64
+    bf16 blocks per (batch, head) pair of a pass, holding a key block's query blocks from its first
+    causally visible one on."""
     L = _lib()
-    base = L.lwm_blockattn_bwd_workspace_size(2, 3, 300, 500, 128)
-    slot = 512 * 512 * 2
-    assert L.lwm_blockattn_bwd_workspace_size_ds(2, 3, 300, 500, 128, 4) == base + 4 * slot
-    assert L.lwm_blockattn_bwd_workspace_size_ds(2, 3, 300, 500, 128, 100) == base + 6 * slot  # clamped to B*H
-    assert L.lwm_blockattn_bwd_workspace_size_ds(1, 1, 256, 7, 128, 1) == L.lwm_blockattn_bwd_workspace_size(
-        1, 1, 256, 7, 128) + 64 * 256 * 2
-    for args in ((2, 3, 300, 500, 128, 0), (2, 3, 300, 500, 128, -5), (2, 3, 300, 0, 128, 4),
-                 (1, 1, (1 << 21) + 1, 64, 128, 1)):
+    cases = [(300, 500, 0, 0, 1), (300, 500, 0, 0, 0), (256, 7, 0, 0, 1), (1000, 1000, 180, 0, 1),
+             (400, 380, 0, 100, 1), (300, 600, 10000, 9800, 1), (260, 200, 5000, 0, 1), (64, 640, 0, 300, 1),
+             (32768, 32768, 0, 0, 1), (16384, 16384, 16384 * 40, 16384 * 40, 1), (16384, 16384, 0, 16384, 1),
+             (65536, 65536, 0, 0, 1), (1, 1, 0, 0, 1), (1, 1, 0, 63, 1), (5, 64, 64, 0, 1)]
+    for Lq, Lk, qo, ko, causal in cases:
+        base = L.lwm_blockattn_bwd_workspace_size(2, 3, Lq, Lk, 128)
+        slot = ds_blocks_brute(Lq, Lk, qo, ko, causal) * 8192
+        for heads in (1, 4, 100):
+            got = L.lwm_blockattn_bwd_workspace_size_ds(2, 3, Lq, Lk, 128, qo, ko, causal, heads)
+            want = base + min(heads, 6) * slot if slot else base
+            assert got == want, (Lq, Lk, qo, ko, causal, heads, got, want)
+    # a causal square slot keeps the blocks on and after the diagonal: 8 + 7 + ... + 1 of 8 x 8
+    assert ds_blocks_brute(300, 500, 0, 0, 1) == 36 and ds_blocks_brute(300, 500, 0, 0, 0) == 64
+    assert ds_blocks_brute(256, 7, 0, 0, 1) == 4  # 256 queries = 4 blocks, one key block
+    assert ds_blocks_brute(16384, 16384, 0, 16384, 1) == 0  # keys all after the queries
+    for args in ((2, 3, 300, 500, 128, 0, 0, 1, 0), (2, 3, 300, 500, 128, 0, 0, 1, -5),
+                 (2, 3, 300, 0, 128, 0, 0, 1, 4), (1, 1, (1 << 21) + 1, 64, 128, 0, 0, 1, 1),
+                 (1, 1, 64, 64, 128, -1, 0, 1, 1), (1, 1, 64, 64, 128, 0, (1 << 40) + 1, 1, 1),
+                 (1, 1, 16384, 16384, 128, 0, 16384, 1, 1)):
         assert L.lwm_blockattn_bwd_workspace_size_ds(*args) == L.lwm_blockattn_bwd_workspace_size(*args[:5]), args
-    assert L.lwm_blockattn_bwd_workspace_size_ds(0, 3, 300, 500, 128, 4) == 256
-    assert L.lwm_blockattn_bwd_workspace_size_ds(64, 64, 1 << 21, 1 << 31, 128, 4096) == 2**64 - 1
+    assert L.lwm_blockattn_bwd_workspace_size_ds(0, 3, 300, 500, 128, 0, 0, 1, 4) == 256
+    assert L.lwm_blockattn_bwd_workspace_size_ds(64, 64, 1 << 21, 1 << 31, 128, 0, 0, 0, 4096) == 2**64 - 1
 
 
 def test_default_stored_ds_heads():
-    """The binding's choice of pairs per pass for the workspaces it allocates (64 GiB of dS)."""
-    assert lwm.DS_BUDGET_BYTES == 64 << 30
-    assert lwm.default_ds_heads(1, 32, 32768, 32768, 128) == 32  # 32 slots of 2 GiB
-    assert lwm.default_ds_heads(1, 32, 65536, 65536, 128) == 0  # 8 GiB slots: 8 per pass, under 16
-    assert lwm.default_ds_heads(1, 32, 65536, 65536, 128, budget=130 << 30) == 16  # a multiple of 8
+    """The binding's choice of pairs per pass for the workspaces it allocates (up to 80 GiB of dS)."""
+    assert lwm.DS_BUDGET_BYTES == 80 << 30
+    assert lwm.default_ds_heads(1, 32, 32768, 32768, 128) == 32  # causal slots of about 1 GiB
+    assert lwm.default_ds_heads(1, 32, 32768, 32768, 128, causal=False) == 32  # 2 GiB each
+    assert lwm.default_ds_heads(1, 32, 65536, 65536, 128) == 16  # 4.3 GB slots: 19, then a multiple of 8
+    assert lwm.default_ds_heads(1, 32, 65536, 65536, 128, causal=False) == 0  # 8 GiB slots: 8, under 16
     assert lwm.default_ds_heads(1, 4, 1 << 20, 1 << 20, 128) == 0  # not one slot fits
-    slot = 4096 * 4096 * 2
+    slot = lwm.lwm_blockattn_bwd_workspace_size_ds(1, 1, 4096, 4096, 128, 1) - \
+        lwm.lwm_blockattn_bwd_workspace_size(1, 1, 4096, 4096, 128)
+    assert slot == 64 * 65 // 2 * 8192
     assert lwm.default_ds_heads(1, 12, 4096, 4096, 128, budget=12 * slot) == 12
     assert lwm.default_ds_heads(1, 12, 4096, 4096, 128, budget=11 * slot) == 0
     assert lwm.default_ds_heads(1, 40, 4096, 4096, 128, budget=39 * slot) == 32

@@ -17,10 +17,24 @@ from tests.gpu_utils import GRAD_REL_FRO, dev, exact_host, host, need_gpu, note,
 pytestmark = pytest.mark.gpu
 
 
-def poisoned_workspace(B, H, Lq, Lk, ds_heads):
-    ws = lwm.bwd_workspace(B, H, Lq, Lk, 128, "cuda", ds_heads)
+def poisoned_workspace(B, H, Lq, Lk, ds_heads, q_offset=0, k_offset=0, causal=True):
+    ws = lwm.bwd_workspace(B, H, Lq, Lk, 128, "cuda", ds_heads, q_offset, k_offset, causal)
     ws.fill_(255)
     return ws
+
+
+def stored_launches(fn):
+    """Run fn with the library's launch timing on; return how many dQ-from-dS launches it made (the
+    stored-dS path must really run where a test means it to)."""
+    lwm.lwm_profile_reset()
+    lwm.lwm_profile_enable(True)
+    try:
+        out = fn()
+        torch.cuda.synchronize()
+        prof = lwm.lwm_profile_read()
+    finally:
+        lwm.lwm_profile_enable(False)
+    return out, prof.get("bwd_dq_ds", (0.0, 0))[1]
 
 
 def inputs(B, Lq, Lk, H, seed, segs):
@@ -45,10 +59,13 @@ def stored_vs_recomputed(B, Lq, Lk, H, seed, segs=False, q_offset=0, k_offset=0,
                                 workspace=lwm.bwd_workspace(B, H, Lq, Lk, 128, "cuda", 0))
     got = None
     for g in heads:
-        assert (lwm.default_ds_heads(B, H, Lq, Lk, 128) if g is None else g) > 0
-        got = lwm.lwm_blockattn_bwd(qd, kd, vd, o, lse, dod, sqd, skd, q_offset, k_offset, causal,
-                                    workspace=poisoned_workspace(B, H, Lq, Lk, g))
-        torch.cuda.synchronize()
+        per_pass = lwm.default_ds_heads(B, H, Lq, Lk, 128, q_offset=q_offset, k_offset=k_offset,
+                                        causal=causal) if g is None else g
+        assert per_pass > 0
+        ws = poisoned_workspace(B, H, Lq, Lk, g, q_offset, k_offset, causal)
+        got, n = stored_launches(lambda: lwm.lwm_blockattn_bwd(qd, kd, vd, o, lse, dod, sqd, skd, q_offset, k_offset,
+                                                               causal, workspace=ws))
+        assert n == -(-(B * H) // per_pass), (n, per_pass)
         for name, a, r in zip(("dq", "dk", "dv"), got, ref):
             assert torch.equal(a, r), (name, g, float((a.float() - r.float()).abs().max()))
     rdq, rdk, rdv = oracle.attention_bwd(exact_host(q, "bf16"), exact_host(k, "bf16"), exact_host(v, "bf16"),
@@ -74,7 +91,8 @@ def test_noncausal_rectangular():
 
 
 @pytest.mark.parametrize("q_offset,k_offset,Lq,Lk", [(180, 0, 520, 700), (0, 100, 400, 380),
-                                                      (10000, 9800, 300, 600), (5000, 0, 260, 200)])
+                                                      (10000, 9800, 300, 600), (5000, 0, 260, 200),
+                                                      (0, 30, 64, 640), (37, 0, 300, 300)])
 def test_causal_offsets(q_offset, k_offset, Lq, Lk):
     stored_vs_recomputed(1, Lq, Lk, 2, 21 + Lq, q_offset=q_offset, k_offset=k_offset)
 
@@ -103,9 +121,9 @@ def test_rope_fused_backward():
     o, lse, q_rot, k_rot = lwm.lwm_blockattn_fwd_rope(qd, kd, vd, 1e6)
     ref = lwm.lwm_blockattn_bwd_rope(q_rot, k_rot, vd, o, lse, dod, 1e6,
                                      workspace=lwm.bwd_workspace(B, H, L, L, 128, "cuda", 0))
-    got = lwm.lwm_blockattn_bwd_rope(q_rot, k_rot, vd, o, lse, dod, 1e6,
-                                     workspace=poisoned_workspace(B, H, L, L, None))
-    torch.cuda.synchronize()
+    ws = poisoned_workspace(B, H, L, L, None)
+    got, n = stored_launches(lambda: lwm.lwm_blockattn_bwd_rope(q_rot, k_rot, vd, o, lse, dod, 1e6, workspace=ws))
+    assert n == 1
     for name, a, r in zip(("dq", "dk", "dv"), got, ref):
         assert torch.equal(a, r), name
 
@@ -129,9 +147,10 @@ def test_ring_backward_stored_ds(segs):
     o, _, lse = path.ring_forward(qd, kd, vd, order, S, q_off, seg_q=sqd, seg_k_shards=skd)
     ref = path.ring_backward(qd, kd, vd, o, lse, dod, order, S, q_off, seg_q=sqd, seg_k_shards=skd,
                              workspace=lwm.bwd_workspace(1, H, Lq, S, 128, "cuda", 0))
-    got = path.ring_backward(qd, kd, vd, o, lse, dod, order, S, q_off, seg_q=sqd, seg_k_shards=skd,
-                             workspace=poisoned_workspace(1, H, Lq, S, None))
-    torch.cuda.synchronize()
+    ws = poisoned_workspace(1, H, Lq, S, None, causal=False)
+    got, n = stored_launches(lambda: path.ring_backward(qd, kd, vd, o, lse, dod, order, S, q_off, seg_q=sqd,
+                                                        seg_k_shards=skd, workspace=ws))
+    assert n == 4  # every shard is visible to the block (it sits after them all)
     assert torch.equal(got[0], ref[0]), "dq"
     for j in range(n):
         assert torch.equal(got[1][j], ref[1][j]), ("dk", j)
@@ -149,7 +168,8 @@ def test_small_workspace_takes_the_recomputing_path():
     o, lse = lwm.lwm_blockattn_fwd(qd, kd, vd)
     full = lwm.lwm_blockattn_bwd_workspace_size_ds(B, H, L, L, 128, H)
     ws = torch.full((full - 1,), 255, dtype=torch.uint8, device="cuda")
-    got = lwm.lwm_blockattn_bwd(qd, kd, vd, o, lse, dod, workspace=ws)
+    got, n = stored_launches(lambda: lwm.lwm_blockattn_bwd(qd, kd, vd, o, lse, dod, workspace=ws))
+    assert n == 0
     ref = lwm.lwm_blockattn_bwd(qd, kd, vd, o, lse, dod, workspace=lwm.bwd_workspace(B, H, L, L, 128, "cuda", 0))
     torch.cuda.synchronize()
     for name, a, r in zip(("dq", "dk", "dv"), got, ref):
