@@ -7,7 +7,10 @@
 //     delta_i = sum_d dO_id O_id
 //     dV = P^T dO,   dP = dO V^T,   dS = P o (dP - delta),   dQ = scale dS K,   dK = scale dS^T Q.
 //
-// Three kernels, no atomics (the result is deterministic):
+// No atomics (the result is deterministic).  With room for it in the workspace the backward stores
+// dS: the dK/dV kernel below also writes dS^T (bf16) and a dQ kernel forms dQ = scale dS K from it
+// (five products in all); otherwise the dQ kernel recomputes S and dP itself (seven).  The two
+// paths give the same bits.  Kernels:
 //  * delta: one pass over dO and O (HBM-bound); also stores lse * log2(e) for the other two.
 //  * dQ: a workgroup per 128-query tile walks the visible 64-key tiles like the forward does,
 //    with scores transposed (S^T = K Q^T) so each lane owns one query: P^T and dS^T are formed in
@@ -20,9 +23,10 @@
 //  With fused RoPE (lwm_blockattn_bwd_rope) the dQ and dK/dV kernels rotate their float32 dQ', dK'
 //  accumulators back by -angle just before the one rounding to bf16, so the stored gradients are
 //  w.r.t. the pre-RoPE Q and K.
-//  Tiles travel HBM -> LDS by buffer loads that write LDS directly (double-buffered).  Recomputing
-//  S and dP in both kernels costs two extra products over the five the method needs; in exchange
-//  no partial dQ is ever written to or reduced through memory.
+//  * dQ from the stored dS: a workgroup per 256-query tile streams K and dS^T tiles through LDS
+//    and forms dQ^T += K^T dS^T only (bound by memory: two bytes of dS per visible pair).
+//  Tiles travel HBM -> LDS by buffer loads that write LDS directly.  Neither path writes or
+//  reduces a partial dQ through memory.
 
 #include <cstddef>
 #include <type_traits>
