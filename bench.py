@@ -226,6 +226,17 @@ def bench_extras(torch, lwm, path, workloads, configs, steps=3, warmup=1):
                               "pct_of_bf16_peak": 100 * tflop / ms / 1e9 / configs.PEAK_BF16_TFLOPS,
                               "attn_bwd_ms": bk, "attn_bwd_tflops": 10 * w.D * w.visible_pairs() / bk / 1e9,
                               "tokens_per_s": w.B * w.Lq / (ms * 1e-3), "steps": n, "warmup": nw, "kernels": ks}
+
+    # the same step through the fused-RoPE calls (positions restart per segment inside the kernels)
+    def packed_train_step_fused():
+        path.training_step_fused(d["q"], d["k"], d["v"], do, w.theta, seg=d["seg"], buffers=bufs)
+
+    ms, prof, n, nw = time_settled(packed_train_step_fused, steps, warmup, lwm, torch)
+    ks = kernels_table(prof, n)
+    out[w.name + "_train"]["rope_fused"] = {
+        "ms_per_step": ms, "tflops": tflop / ms / 1e9, "pct_of_bf16_peak": 100 * tflop / ms / 1e9 / configs.PEAK_BF16_TFLOPS,
+        "tokens_per_s": w.B * w.Lq / (ms * 1e-3), "steps": n, "warmup": nw, "kernels": ks,
+        "note": "same workload and flop count; one RoPE pass (K) instead of four"}
     del d, qr, kr, o, lse, do, bufs
     torch.cuda.empty_cache()
 
